@@ -1,0 +1,54 @@
+"""Pins of the oracle's reported quantities: compression (closed form, and the
+page's printed column) and MAE (trend only: parity unpinned)."""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _page_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "page_quant_table.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            mode, g, mae, comp = line.split()
+            rows.append((mode, None if g == "-" else int(g), float(mae), float(comp)))
+    return rows
+
+
+def test_page_compression_column_reproduced():
+    # The page's column is 16 bits of metadata per group on a 4096 x 4096 matrix.
+    N = K = 4096
+    for mode, g, _, comp in _page_table():
+        pairs = 1 if mode == "GLOBAL" else (N if mode == "ROWWISE" else N * K // g)
+        assert round(O.page_compression_ratio(N, K, pairs), 6) == pytest.approx(comp, abs=1.5e-6)
+
+
+@pytest.mark.parametrize("g", [16, 32, 64, 128, 256, 512, 1024, 2048])
+def test_compression_closed_form(g):
+    N, K = 128, 4096
+    assert O.compression_ratio(N, K, N * K // g) == pytest.approx(16.0 / (4.0 + 32.0 / g), rel=1e-15)
+
+
+def test_mae_trend_matches_page():
+    # The page's MAE grows with the group size and GLOBAL is the worst; the data it was
+    # measured on is unstated, so only the ordering is pinned.
+    N, K = 256, 4096
+    w = synth.weight(300, 0, N, K, "f16", std=1.0)
+    w32 = O.to_f32(w, "f16")
+    maes = {}
+    for g in (16, 32, 64, 128, 256, 512, 1024, 2048, 4096):
+        maes[g] = O.mae(w32, *O.quantize_pack(w32, O.GROUPWISE, g))
+    glob = O.mae(w32, *O.quantize_pack(w32, O.GLOBAL))
+    row = O.mae(w32, *O.quantize_pack(w32, O.ROWWISE))
+    seq = [maes[g] for g in sorted(maes)]
+    assert all(a < b for a, b in zip(seq, seq[1:]))
+    assert glob > max(seq)
+    assert row == pytest.approx(maes[4096], rel=1e-12)
