@@ -1,0 +1,230 @@
+// C ABI of the W4A16 library: argument validation, dispatch, error reporting.
+// The declarations and the contract of every entry point are in include/w4a16.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return W4_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_desc(const w4_desc* d) {
+  if (d == nullptr) return fail(W4_ERR_INVALID, "desc is NULL");
+  if (d->N < 1) return fail(W4_ERR_INVALID, "N = %lld must be >= 1", (long long)d->N);
+  if (d->K < 8 || d->K % 8 != 0) return fail(W4_ERR_INVALID, "K = %lld must be a positive multiple of 8", (long long)d->K);
+  if (d->N > ((int64_t)1 << 31) - 1 || d->K > ((int64_t)1 << 31) - 1)
+    return fail(W4_ERR_UNSUPPORTED, "N and K must fit in int32");
+  if (d->N * (d->K / 8) > ((int64_t)1 << 40)) return fail(W4_ERR_UNSUPPORTED, "matrix too large");
+  switch (d->mode) {
+    case W4_MODE_GLOBAL:
+    case W4_MODE_ROWWISE:
+      break;
+    case W4_MODE_GROUPWISE:
+      if (!is_pow2(d->group) || d->group < 16 || d->group > 4096)
+        return fail(W4_ERR_INVALID, "group = %d must be a power of two in [16, 4096]", d->group);
+      if (d->group > d->K || d->K % d->group != 0)
+        return fail(W4_ERR_INVALID, "group = %d must divide K = %lld", d->group, (long long)d->K);
+      break;
+    default:
+      return fail(W4_ERR_INVALID, "mode = %d is not GLOBAL, ROWWISE or GROUPWISE", d->mode);
+  }
+  return W4_OK;
+}
+
+int64_t pairs_of(const w4_desc* d) {
+  if (d->mode == W4_MODE_GLOBAL) return 1;
+  if (d->mode == W4_MODE_ROWWISE) return d->N;
+  return d->N * (d->K / d->group);
+}
+
+size_t device_lds_limit() {
+  static std::atomic<long long> cached{-1};
+  long long v = cached.load();
+  if (v < 0) {
+    int dev = 0, bytes = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      bytes = 64 * 1024;
+    v = bytes;
+    cached.store(v);
+  }
+  return (size_t)v;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W4_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+             const w4_desc* desc, int transposed, const float* bias, const float* Y) {
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (M < 0) return fail(W4_ERR_INVALID, "M = %lld must be >= 0", (long long)M);
+  if (M > ((int64_t)1 << 31) - 1) return fail(W4_ERR_UNSUPPORTED, "M must fit in int32");
+  if (M == 0) return W4_OK;
+  if (!A || !packed || !scales || !zeros || !Y) return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  if (desc->K % 32 != 0) return fail(W4_ERR_UNSUPPORTED, "matmul needs K %% 32 == 0 (K = %lld)", (long long)desc->K);
+  if (transposed && desc->N % 8 != 0)
+    return fail(W4_ERR_UNSUPPORTED, "transposed matmul needs N %% 8 == 0 (N = %lld)", (long long)desc->N);
+  if (!aligned(A, 16) || !aligned(packed, 16)) return fail(W4_ERR_ALIGN, "A and packed must be 16-byte aligned");
+  if (!aligned(Y, 4) || (bias && !aligned(bias, 4)) || !aligned(scales, 2) || !aligned(zeros, 2))
+    return fail(W4_ERR_ALIGN, "Y / bias must be 4-byte and scales / zeros 2-byte aligned");
+  return W4_OK;
+}
+
+w4::MmArgs make_args(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
+                     const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias, float* Y) {
+  w4::MmArgs a;
+  a.A = A;
+  a.packed = packed;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.bias = bias;
+  a.Y = Y;
+  a.M = M;
+  a.N = desc->N;
+  a.K = desc->K;
+  a.mode = desc->mode;
+  a.group = desc->mode == W4_MODE_GROUPWISE ? desc->group : (int)desc->K;
+  a.transposed = transposed != 0;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4_meta_pairs(const w4_desc* desc, int64_t* pairs) {
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (!pairs) return fail(W4_ERR_INVALID, "pairs is NULL");
+  *pairs = pairs_of(desc);
+  return ok();
+}
+
+int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (!bytes) return fail(W4_ERR_INVALID, "bytes is NULL");
+  (void)M;
+  switch (op) {
+    case W4_OP_QUANTIZE: *bytes = w4::quantize_workspace_bytes(desc->mode); break;
+    case W4_OP_MM:
+    case W4_OP_MM_T:
+    case W4_OP_DEQUANTIZE: *bytes = 0; break;
+    default: return fail(W4_ERR_INVALID, "op = %d is unknown", op);
+  }
+  return ok();
+}
+
+int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc, int32_t* packed, uint16_t* scales,
+                     uint16_t* zeros, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (w_dtype != W4_DT_F32 && w_dtype != W4_DT_F16 && w_dtype != W4_DT_BF16)
+    return fail(W4_ERR_INVALID, "w_dtype = %d is not F32, F16 or BF16", w_dtype);
+  if (!W || !packed || !scales || !zeros) return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned(W, 16)) return fail(W4_ERR_ALIGN, "W must be 16-byte aligned");
+  if (!aligned(packed, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
+    return fail(W4_ERR_ALIGN, "packed must be 4-byte, scales / zeros 2-byte aligned");
+  const size_t need = w4::quantize_workspace_bytes(desc->mode);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(W4_ERR_RESOURCE, "GLOBAL mode needs a workspace of %zu bytes (got %zu)", need, ws_bytes);
+    if (!aligned(ws, 8)) return fail(W4_ERR_ALIGN, "workspace must be 8-byte aligned");
+  }
+  const int g = desc->mode == W4_MODE_GROUPWISE ? desc->group : (int)desc->K;
+  return launched(w4::launch_quantize(W, w_dtype, desc->N, desc->K, desc->mode, g, packed, scales, zeros, ws,
+                                      static_cast<hipStream_t>(stream)),
+                  "quantize_pack");
+}
+
+int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros, const w4_desc* desc,
+                  void* out, int out_dtype, void* stream) {
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (out_dtype != W4_DT_BF16 && out_dtype != W4_DT_F32)
+    return fail(W4_ERR_INVALID, "out_dtype = %d must be BF16 or F32", out_dtype);
+  if (!packed || !scales || !zeros || !out) return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  if (!aligned(out, 16) || !aligned(packed, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
+    return fail(W4_ERR_ALIGN, "out must be 16-byte, packed 4-byte, scales / zeros 2-byte aligned");
+  const int g = desc->mode == W4_MODE_GROUPWISE ? desc->group : (int)desc->K;
+  return launched(w4::launch_dequantize(packed, scales, zeros, desc->N, desc->K, desc->mode, g, out, out_dtype,
+                                        static_cast<hipStream_t>(stream)),
+                  "dequantize");
+}
+
+int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+             const w4_desc* desc, int transposed, const float* bias, float* Y, void* ws, size_t ws_bytes,
+             void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int s = check_mm(A, M, packed, scales, zeros, desc, transposed, bias, Y);
+  if (s != W4_OK) return s;
+  if (M == 0) return ok();
+  const w4::MmArgs a = make_args(A, M, packed, scales, zeros, desc, transposed, bias, Y);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (w4::gemv_supported(a, device_lds_limit())) return launched(w4::launch_gemv(a, st), "gemv");
+  if (w4::gemm_lds_bytes(a) > device_lds_limit())
+    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a),
+                device_lds_limit());
+  return launched(w4::launch_gemm(a, st), "gemm");
+}
+
+const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
+  // validation without pointers: use a dummy aligned address
+  static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
+  const void* p = dummy;
+  int s = check_mm(static_cast<const uint16_t*>(p), M, static_cast<const int32_t*>(p), dummy, dummy, desc,
+                   transposed, nullptr, reinterpret_cast<const float*>(p));
+  if (s != W4_OK || M == 0) return nullptr;
+  const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, nullptr,
+                                 nullptr);
+  if (w4::gemv_supported(a, device_lds_limit())) return w4::gemv_name(a);
+  return w4::gemm_name(a);
+}
+
+const char* w4_status_string(int status) {
+  switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_ERR_INVALID: return "W4_ERR_INVALID";
+    case W4_ERR_UNSUPPORTED: return "W4_ERR_UNSUPPORTED";
+    case W4_ERR_ALIGN: return "W4_ERR_ALIGN";
+    case W4_ERR_RESOURCE: return "W4_ERR_RESOURCE";
+    case W4_ERR_LAUNCH: return "W4_ERR_LAUNCH";
+  }
+  return "W4_ERR_UNKNOWN";
+}
+
+const char* w4_last_error(void) { return g_last_error.c_str(); }
+
+const char* w4_version(void) { return "w4a16-gfx950 0.1.0"; }
+
+}  // extern "C"

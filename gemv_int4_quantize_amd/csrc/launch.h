@@ -1,0 +1,44 @@
+// Internal launchers of the W4A16 library (host side).  Arguments are validated
+// by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/w4a16.h"
+
+namespace w4 {
+
+hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+                           uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st);
+size_t quantize_workspace_bytes(int mode);
+
+hipError_t launch_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                             int64_t K, int mode, int g, void* out, int out_dt, hipStream_t st);
+
+// Matmul problem after validation: A [M][L] bf16 (L = contraction), packed [N][K/8].
+struct MmArgs {
+  const uint16_t* A;
+  const int32_t* packed;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const float* bias;
+  float* Y;
+  int64_t M, N, K;
+  int mode;   // w4_mode
+  int group;  // GROUPWISE g, else K
+  bool transposed;
+};
+
+// GEMV (M <= 4, non-transposed).  Returns false if this shape cannot run on it
+// (LDS footprint), so the caller can fall back to the GEMM.
+bool gemv_supported(const MmArgs& a, size_t lds_limit);
+const char* gemv_name(const MmArgs& a);
+hipError_t launch_gemv(const MmArgs& a, hipStream_t st);
+
+const char* gemm_name(const MmArgs& a);
+size_t gemm_lds_bytes(const MmArgs& a);
+hipError_t launch_gemm(const MmArgs& a, hipStream_t st);
+
+}  // namespace w4

@@ -1,0 +1,329 @@
+// Quantize-and-pack and dequantize kernels for gfx950.
+//
+// Method: Objective 1 of "Quantized LLM Inference with Triton Kernels"
+// (anaaaiva/llm-quantization): FP16 -> INT4 with one scale and zero per group
+// (global, rowwise or groupwise along K), packed 8 codes per INT32 word.
+// Per group:  s = fp16_rne((max - min) / 15)  (1 if that is 0 or not finite),
+//             z = fp16_rne((0 - min) / s),
+//             q = clamp(rint(w / s + z), 0, 15),
+// every step in IEEE fp32 (correctly rounded division, no contraction).
+//
+// The kernels are HBM streams: each lane reads the 8 elements of one output word
+// with 16-byte loads (32 for fp32) and writes one int32 word.
+#include "common.h"
+#include "launch.h"
+
+namespace w4 {
+
+// 8 consecutive elements of W starting at element `off`, widened to fp32 (exact).
+template <int DT>
+__device__ __forceinline__ void load8(const void* W, int64_t off, float v[8]) {
+  if constexpr (DT == W4_DT_F32) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(W) + off);
+    const f32x4 a = p[0];
+    const f32x4 b = p[1];
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == W4_DT_F16) {
+        v[2 * i] = f16_bits_to_f32(u[i] & 0xFFFFu);
+        v[2 * i + 1] = f16_bits_to_f32(u[i] >> 16);
+      } else {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+struct QParams {
+  float s, z;        // fp32 values of the fp16 scale and zero
+  uint16_t sb, zb;   // their fp16 bits
+};
+
+__device__ __forceinline__ QParams qparams(float lo, float hi) {
+  const float s32 = (hi - lo) / 15.0f;
+  uint16_t sb = f32_to_f16_bits(s32);
+  float s = f16_bits_to_f32(sb);
+  if (!(s != 0.0f) || !__builtin_isfinite(s)) {
+    sb = 0x3C00;  // 1.0
+    s = 1.0f;
+  }
+  // IEEE 0 - lo is +0 when lo is +0 or -0 and -lo otherwise.  Written as a select: the
+  // backend turns `0.0f - lo` into a negate modifier, which yields -0 for lo == +0.
+  const float nlo = lo == 0.0f ? 0.0f : -lo;
+  const float z32 = nlo / s;
+  const uint16_t zb = f32_to_f16_bits(z32);
+  QParams p;
+  p.s = s;
+  p.z = f16_bits_to_f32(zb);
+  p.sb = sb;
+  p.zb = zb;
+  return p;
+}
+
+__device__ __forceinline__ uint32_t code4(float w, const QParams& p) {
+  const float t = w / p.s + p.z;  // IEEE divide, then add
+  const float r = __builtin_rintf(t);  // round half to even
+  return (uint32_t)__builtin_fminf(__builtin_fmaxf(r, 0.0f), 15.0f);
+}
+
+__device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= code4(v[j], p) << (4 * j);
+  return w;
+}
+
+// Groups of T * 8 elements (T lanes, T | 64, one word per lane).  Groups tile the
+// rows exactly, so group index = global word index / T.
+template <int DT, int T>
+__global__ __launch_bounds__(256) void quant_small_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
+                                                          uint16_t* __restrict__ scales,
+                                                          uint16_t* __restrict__ zeros, int64_t total_words) {
+  const int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = gw < total_words;
+  float v[8];
+  if (valid) {
+    load8<DT>(W, gw * 8, v);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+  }
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) {
+    lo = __builtin_fminf(lo, v[j]);
+    hi = __builtin_fmaxf(hi, v[j]);
+  }
+#pragma unroll
+  for (int o = T / 2; o >= 1; o >>= 1) {
+    lo = __builtin_fminf(lo, __shfl_xor(lo, o));
+    hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
+  }
+  const QParams p = qparams(lo, hi);
+  const uint32_t word = pack8(v, p);
+  if (valid) {
+    packed[gw] = (int32_t)word;
+    if ((threadIdx.x & (T - 1)) == 0) {
+      scales[gw / T] = p.sb;
+      zeros[gw / T] = p.zb;
+    }
+  }
+}
+
+// One wave per group of `wpg` words (large groups, ROWWISE with long rows):
+// pass 1 reduces min / max, pass 2 re-reads the group (an L2 hit) and packs.
+template <int DT>
+__global__ __launch_bounds__(256) void quant_large_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
+                                                          uint16_t* __restrict__ scales,
+                                                          uint16_t* __restrict__ zeros, int64_t num_groups,
+                                                          int wpg) {
+  const int lane = threadIdx.x & 63;
+  const int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (grp >= num_groups) return;
+  const int64_t w0 = grp * wpg;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int c = lane; c < wpg; c += kWave) {
+    float v[8];
+    load8<DT>(W, (w0 + c) * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo = __builtin_fminf(lo, v[j]);
+      hi = __builtin_fmaxf(hi, v[j]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = __builtin_fminf(lo, __shfl_xor(lo, o));
+    hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
+  }
+  const QParams p = qparams(lo, hi);
+  for (int c = lane; c < wpg; c += kWave) {
+    float v[8];
+    load8<DT>(W, (w0 + c) * 8, v);
+    packed[w0 + c] = (int32_t)pack8(v, p);
+  }
+  if (lane == 0) {
+    scales[grp] = p.sb;
+    zeros[grp] = p.zb;
+  }
+}
+
+constexpr int kMinMaxBlocks = 1024;
+
+__device__ __forceinline__ void block_minmax(float& lo, float& hi) {
+  __shared__ float red_lo[4], red_hi[4];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = __builtin_fminf(lo, __shfl_xor(lo, o));
+    hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
+  }
+  const int wid = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red_lo[wid] = lo;
+    red_hi[wid] = hi;
+  }
+  __syncthreads();
+  lo = __builtin_fminf(__builtin_fminf(red_lo[0], red_lo[1]), __builtin_fminf(red_lo[2], red_lo[3]));
+  hi = __builtin_fmaxf(__builtin_fmaxf(red_hi[0], red_hi[1]), __builtin_fmaxf(red_hi[2], red_hi[3]));
+}
+
+// GLOBAL pass 1: per-block min / max over a grid-stride range of words.
+template <int DT>
+__global__ __launch_bounds__(256) void minmax_partial_kernel(const void* __restrict__ W, int64_t total_words,
+                                                             float* __restrict__ partial) {
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x; gw < total_words; gw += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8<DT>(W, gw * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo = __builtin_fminf(lo, v[j]);
+      hi = __builtin_fmaxf(hi, v[j]);
+    }
+  }
+  block_minmax(lo, hi);
+  if (threadIdx.x == 0) {
+    partial[2 * blockIdx.x] = lo;
+    partial[2 * blockIdx.x + 1] = hi;
+  }
+}
+
+// GLOBAL pass 2: every block folds the partials (min / max are exact, so every
+// block derives the same scale and zero), then packs a grid-stride range.
+template <int DT>
+__global__ __launch_bounds__(256) void quant_global_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
+                                                           uint16_t* __restrict__ scales,
+                                                           uint16_t* __restrict__ zeros, int64_t total_words,
+                                                           const float* __restrict__ partial, int nparts) {
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    lo = __builtin_fminf(lo, partial[2 * i]);
+    hi = __builtin_fmaxf(hi, partial[2 * i + 1]);
+  }
+  block_minmax(lo, hi);
+  const QParams p = qparams(lo, hi);
+  for (int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x; gw < total_words; gw += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8<DT>(W, gw * 8, v);
+    packed[gw] = (int32_t)pack8(v, p);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scales[0] = p.sb;
+    zeros[0] = p.zb;
+  }
+}
+
+// Dequantize: bf16_rne(fp32(q - z) * s) or fp32(q - z) * s, the exact two-op
+// sequence (subtract, then multiply, each rounded) of the reference definition.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict__ packed,
+                                                      const uint16_t* __restrict__ scales,
+                                                      const uint16_t* __restrict__ zeros, void* __restrict__ out,
+                                                      int64_t total_words, int64_t words_per_row, int meta_kind,
+                                                      int64_t groups_per_row, int words_per_group) {
+  const int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gw >= total_words) return;
+  int64_t mi = 0;
+  if (meta_kind != META_GLOBAL) {
+    const int64_t n = gw / words_per_row;
+    mi = meta_kind == META_ROW ? n : n * groups_per_row + (gw - n * words_per_row) / words_per_group;
+  }
+  const float s = f16_bits_to_f32(scales[mi]);
+  const float z = f16_bits_to_f32(zeros[mi]);
+  const uint32_t w = (uint32_t)packed[gw];
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float qf = (float)((w >> (4 * j)) & 0xFu);
+    const float d = qf - z;
+    v[j] = d * s;
+  }
+  if constexpr (BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + gw);
+  } else {
+    f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    f32x4* p = reinterpret_cast<f32x4*>(out) + 2 * gw;
+    __builtin_nontemporal_store(a, p);
+    __builtin_nontemporal_store(b, p + 1);
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int DT>
+static hipError_t quant_small_dispatch(int T, const void* W, int32_t* packed, uint16_t* scales, uint16_t* zeros,
+                                       int64_t total_words, hipStream_t st) {
+  const dim3 grid((unsigned)((total_words + 255) / 256)), block(256);
+  switch (T) {
+    case 2: quant_small_kernel<DT, 2><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 4: quant_small_kernel<DT, 4><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 8: quant_small_kernel<DT, 8><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 16: quant_small_kernel<DT, 16><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 32: quant_small_kernel<DT, 32><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 64: quant_small_kernel<DT, 64><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t quantize_dt(const void* W, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+                              uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st) {
+  const int64_t total_words = N * (K / 8);
+  if (mode == W4_MODE_GLOBAL) {
+    float* partial = static_cast<float*>(ws);
+    const int64_t want = (total_words + 255) / 256;
+    const int nb = (int)(want < kMinMaxBlocks ? want : kMinMaxBlocks);
+    minmax_partial_kernel<DT><<<nb, 256, 0, st>>>(W, total_words, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t qb = (total_words + 255) / 256;
+    const int qgrid = (int)(qb < 8192 ? qb : 8192);
+    quant_global_kernel<DT><<<qgrid, 256, 0, st>>>(W, packed, scales, zeros, total_words, partial, nb);
+    return hipGetLastError();
+  }
+  const int64_t gsize = mode == W4_MODE_ROWWISE ? K : g;
+  const int64_t wpg = gsize / 8;
+  if (wpg <= 64 && (wpg & (wpg - 1)) == 0 && wpg >= 2)
+    return quant_small_dispatch<DT>((int)wpg, W, packed, scales, zeros, total_words, st);
+  const int64_t ngroups = total_words / wpg;
+  quant_large_kernel<DT><<<(unsigned)((ngroups + 3) / 4), 256, 0, st>>>(W, packed, scales, zeros, ngroups, (int)wpg);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+                           uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st) {
+  switch (dt) {
+    case W4_DT_F32: return quantize_dt<W4_DT_F32>(W, N, K, mode, g, packed, scales, zeros, ws, st);
+    case W4_DT_F16: return quantize_dt<W4_DT_F16>(W, N, K, mode, g, packed, scales, zeros, ws, st);
+    case W4_DT_BF16: return quantize_dt<W4_DT_BF16>(W, N, K, mode, g, packed, scales, zeros, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t quantize_workspace_bytes(int mode) { return mode == W4_MODE_GLOBAL ? 2 * sizeof(float) * kMinMaxBlocks : 0; }
+
+hipError_t launch_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                             int64_t K, int mode, int g, void* out, int out_dt, hipStream_t st) {
+  const int64_t wpr = K / 8;
+  const int64_t total_words = N * wpr;
+  const int kind = mode == W4_MODE_GLOBAL ? META_GLOBAL : (mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP);
+  const int64_t gpr = mode == W4_MODE_GROUPWISE ? K / g : 1;
+  const int wpgrp = mode == W4_MODE_GROUPWISE ? g / 8 : (int)wpr;
+  const dim3 grid((unsigned)((total_words + 255) / 256)), block(256);
+  if (out_dt == W4_DT_BF16)
+    dequant_kernel<true><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
+  else
+    dequant_kernel<false><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
+  return hipGetLastError();
+}
+
+}  // namespace w4

@@ -1,0 +1,188 @@
+"""PyTorch-facing binding of the W4A16 library.
+
+Argument marshalling only: tensors supply device memory and the current HIP
+stream; every step of quantization, dequantization and the matmul runs in the
+library's gfx950 kernels (see include/w4a16.h for the contract).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import DT_BF16, DT_F16, DT_F32, MODE_GLOBAL, MODE_GROUPWISE, MODE_ROWWISE, W4Desc, check, lib
+
+_MODES = {"global": MODE_GLOBAL, "rowwise": MODE_ROWWISE, "groupwise": MODE_GROUPWISE}
+_WDT = {torch.float32: DT_F32, torch.float16: DT_F16, torch.bfloat16: DT_BF16}
+
+
+def mode_id(mode) -> int:
+    if isinstance(mode, str):
+        return _MODES[mode.lower()]
+    return int(mode)
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _as_bf16(a: torch.Tensor) -> torch.Tensor:
+    """Accept bf16 tensors or 16-bit integer tensors holding bf16 bits."""
+    if a.dtype == torch.bfloat16:
+        return a
+    if a.dtype in (torch.int16, torch.uint16):
+        return a.view(torch.bfloat16)
+    raise TypeError(f"activations must be bfloat16 (got {a.dtype})")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device")
+
+
+@dataclass
+class QuantizedWeight:
+    """Packed int4 weight W[N][K]: packed int32 [N][K/8], fp16 scales / zeros."""
+
+    packed: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor
+    N: int
+    K: int
+    mode: int
+    group: int
+
+    def desc(self) -> W4Desc:
+        return W4Desc(self.N, self.K, self.mode, self.group if self.mode == MODE_GROUPWISE else 0)
+
+    def mm(self, x: torch.Tensor, bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+        """Y = X @ w^T (+ bias)."""
+        return mm(x, self, transposed=False, bias=bias, out=out)
+
+    def mm_t(self, dy: torch.Tensor, bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+        """dX = dY @ w (+ bias), on the same packed buffer."""
+        return mm(dy, self, transposed=True, bias=bias, out=out)
+
+
+def meta_shape(N: int, K: int, mode: int, group: int) -> tuple[int, int]:
+    if mode == MODE_GLOBAL:
+        return (1, 1)
+    if mode == MODE_ROWWISE:
+        return (N, 1)
+    return (N, K // group)
+
+
+def empty_quantized(N: int, K: int, mode, group: int | None, device) -> QuantizedWeight:
+    """Allocate the buffers of a packed weight (contents undefined)."""
+    m = mode_id(mode)
+    g = int(group) if m == MODE_GROUPWISE else 0
+    shp = meta_shape(N, K, m, g)
+    return QuantizedWeight(
+        packed=torch.empty((N, K // 8), dtype=torch.int32, device=device),
+        scales=torch.empty(shp, dtype=torch.float16, device=device),
+        zeros=torch.empty(shp, dtype=torch.float16, device=device),
+        N=N, K=K, mode=m, group=g)
+
+
+def quantize_pack_into(W: torch.Tensor, qw: QuantizedWeight, row0: int = 0) -> None:
+    """Quantize W [n][K] into rows row0 .. row0+n of an existing packed weight.
+
+    Used to fuse projections (for example Q, K and V) into one packed operand
+    without a copy: each part is quantized straight into its row slice.
+    """
+    _need_cuda(W, qw.packed)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
+    n, K = W.shape
+    if K != qw.K or row0 < 0 or row0 + n > qw.N:
+        raise ValueError("W does not fit the packed weight")
+    if qw.mode == MODE_GLOBAL and (row0 != 0 or n != qw.N):
+        raise ValueError("a GLOBAL scale / zero cannot be shared by row slices")
+    dt = _WDT.get(W.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported weight dtype {W.dtype}")
+    desc = W4Desc(n, K, qw.mode, qw.group)
+    L = lib()
+    ws_bytes = ctypes.c_size_t(0)
+    check(L.w4_workspace_bytes(ctypes.byref(desc), _lib.OP_QUANTIZE, 0, ctypes.byref(ws_bytes)))
+    ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=W.device) if ws_bytes.value else None
+    gpr = qw.scales.shape[1]
+    mrow = 0 if qw.mode == MODE_GLOBAL else row0
+    packed = qw.packed[row0:row0 + n]
+    scales = qw.scales[mrow:mrow + (1 if qw.mode == MODE_GLOBAL else n)]
+    zeros = qw.zeros[mrow:mrow + (1 if qw.mode == MODE_GLOBAL else n)]
+    assert scales.shape[1] == gpr
+    check(L.w4_quantize_pack(_ptr(W), dt, ctypes.byref(desc), _ptr(packed), _ptr(scales), _ptr(zeros),
+                             _ptr(ws), ws_bytes.value, _stream(W.device)))
+
+
+def quantize_pack(W: torch.Tensor, mode="groupwise", group: int | None = 128) -> QuantizedWeight:
+    """Quantize and pack W [N][K] (fp32, fp16 or bf16) to asymmetric uint4."""
+    N, K = W.shape
+    qw = empty_quantized(N, K, mode, group, W.device)
+    quantize_pack_into(W, qw, 0)
+    return qw
+
+
+def quantize_fused(parts, mode="groupwise", group: int | None = 128) -> QuantizedWeight:
+    """Quantize several [n_i][K] weights into one row-concatenated packed operand (fused QKV)."""
+    K = parts[0].shape[1]
+    N = sum(p.shape[0] for p in parts)
+    if mode_id(mode) == MODE_GLOBAL:
+        raise ValueError("GLOBAL scale / zero cannot be fused by rows")
+    qw = empty_quantized(N, K, mode, group, parts[0].device)
+    r = 0
+    for p in parts:
+        quantize_pack_into(p, qw, r)
+        r += p.shape[0]
+    return qw
+
+
+def dequantize(qw: QuantizedWeight, dtype=torch.bfloat16) -> torch.Tensor:
+    """w = bf16_rne((q - z) * s) (dtype bfloat16) or fp32 (q - z) * s (dtype float32), [N][K]."""
+    _need_cuda(qw.packed)
+    out = torch.empty((qw.N, qw.K), dtype=dtype, device=qw.packed.device)
+    odt = {torch.bfloat16: DT_BF16, torch.float32: DT_F32}[dtype]
+    desc = qw.desc()
+    check(lib().w4_dequantize(_ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc), _ptr(out), odt,
+                              _stream(out.device)))
+    return out
+
+
+def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: torch.Tensor | None = None,
+       out: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias); fp32 output."""
+    a = _as_bf16(a)
+    _need_cuda(a, qw.packed, bias, out)
+    if a.dim() != 2 or not a.is_contiguous():
+        raise ValueError("activations must be a contiguous 2-D tensor")
+    M, L = a.shape
+    if L != (qw.N if transposed else qw.K):
+        raise ValueError(f"activation width {L} does not match the weight ({qw.N}x{qw.K}, transposed={transposed})")
+    outc = qw.K if transposed else qw.N
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != outc or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous fp32 vector of length {outc}")
+    if out is None:
+        out = torch.empty((M, outc), dtype=torch.float32, device=a.device)
+    elif out.shape != (M, outc) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of the output shape")
+    desc = qw.desc()
+    check(lib().w4a16_mm(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
+                         1 if transposed else 0, _ptr(bias), _ptr(out), None, 0, _stream(a.device)))
+    return out
+
+
+def kernel_for(M: int, N: int, K: int, mode="groupwise", group: int | None = 128, transposed=False) -> str | None:
+    """Name of the kernel the library dispatches for this shape (host-side query)."""
+    m = mode_id(mode)
+    desc = W4Desc(N, K, m, int(group) if m == MODE_GROUPWISE else 0)
+    r = lib().w4a16_mm_kernel(M, ctypes.byref(desc), 1 if transposed else 0)
+    return r.decode() if r is not None else None

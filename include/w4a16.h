@@ -1,0 +1,133 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) weight-only int4 library.
+ *
+ * Two operations, following these pages:
+ *   - "Quantized LLM Inference with Triton Kernels" (anaaaiva/llm-quantization),
+ *     Objectives 1-2: FP16 -> INT4 quantization with global / rowwise /
+ *     groupwise scale and zero, packed into INT32 words; Y = X_bf16 @ W_int4^T.
+ *   - "Re-write HQQ Fused Gemm Transpose" (pytorch/ao #185): the transposed
+ *     product reads the same packed weights, scales and zeros, with no repacking.
+ *   - "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560):
+ *     an optional fp32 bias added in the epilogue.
+ *   - "Modify small-batched weight only quantization" (TensorRT-LLM #2213): the
+ *     batched decode GEMV (M <= 4) at 4 bits with group size 128.
+ *
+ * Data layout (every buffer row-major and contiguous):
+ *   W       [N][K]    fp32, fp16 or bf16 weights to quantize.
+ *   packed  [N][K/8]  int32; code k = 8c + j of row n is bits 4j..4j+3 of word c.
+ *   scales  fp16 bits: GLOBAL [1], ROWWISE [N], GROUPWISE [N][K/g] (group fastest).
+ *   zeros   fp16 bits, same shape as scales.
+ *   A       bf16 bits: X [M][K] (non-transposed) or dY [M][N] (transposed).
+ *   Y       fp32: [M][N] (non-transposed) or [M][K] (transposed).
+ *   bias    fp32, optional: length N (non-transposed) or K (transposed).
+ *
+ * Arithmetic:
+ *   s = fp16_rne((max - min) / 15) per group, replaced by 1 when it is 0 or not
+ *   finite; z = fp16_rne((0 - min) / s); q = clamp(rint(w / s + z), 0, 15), all
+ *   in IEEE fp32.  The matmul weight operand is bf16_rne((q - z) * s) and products
+ *   accumulate in fp32.
+ *
+ * Ownership and execution: every pointer is a device pointer owned by the caller
+ * (except the descriptor and the host out-parameters).  The library never
+ * allocates, frees or synchronizes; work is enqueued on `stream` (a hipStream_t,
+ * 0 = the null stream) and device faults surface at the caller's next
+ * synchronization.  Entry points are thread-safe; the error detail is per thread.
+ *
+ * Errors: arguments are validated on the host before any launch.  On failure an
+ * entry point returns a negative status, enqueues nothing and records a message
+ * readable with w4_last_error().
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_INVALID = -1,     /* bad size, mode, group, null pointer, bias length */
+  W4_ERR_UNSUPPORTED = -2, /* valid but not provided (e.g. matmul with K % 32 != 0) */
+  W4_ERR_ALIGN = -3,       /* a pointer is not aligned as required */
+  W4_ERR_RESOURCE = -4,    /* workspace too small or LDS footprint over the device limit */
+  W4_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
+} w4_status;
+
+typedef enum { W4_MODE_GLOBAL = 0, W4_MODE_ROWWISE = 1, W4_MODE_GROUPWISE = 2 } w4_mode;
+
+typedef enum { W4_DT_F32 = 0, W4_DT_F16 = 1, W4_DT_BF16 = 2 } w4_dtype;
+
+typedef enum { W4_OP_QUANTIZE = 0, W4_OP_MM = 1, W4_OP_MM_T = 2, W4_OP_DEQUANTIZE = 3 } w4_op;
+
+/* Shape and grouping of one quantized weight.  N >= 1 rows, K >= 8 columns,
+ * K % 8 == 0.  `group` is the GROUPWISE group size g along K (a power of two in
+ * [16, 4096] with K % g == 0); it is ignored for GLOBAL and ROWWISE. */
+typedef struct {
+  int64_t N;
+  int64_t K;
+  int32_t mode;  /* w4_mode */
+  int32_t group;
+} w4_desc;
+
+/* Number of (scale, zero) pairs: 1 (GLOBAL), N (ROWWISE), N*K/g (GROUPWISE).
+ * Host only. */
+int w4_meta_pairs(const w4_desc* desc, int64_t* pairs);
+
+/* Device workspace, in bytes, that `op` needs for this descriptor (0 if none);
+ * M is the activation row count for the matmul ops.  Host only. */
+int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes);
+
+/* Quantize and pack W [N][K] (dtype w_dtype) into packed [N][K/8] int32 and the
+ * fp16 scales / zeros.  W must be 16-byte aligned; packed, scales and zeros
+ * 4/2/2-byte aligned.  GLOBAL mode needs the workspace reported by
+ * w4_workspace_bytes (two kernels: a min/max pass, then the quantize pass);
+ * other modes take ws = NULL.  Source: Objective 1 of "Quantized LLM
+ * Inference with Triton Kernels". */
+int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc,
+                     int32_t* packed, uint16_t* scales, uint16_t* zeros,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Dequantize packed weights to out [N][K]: out_dtype W4_DT_BF16 writes the
+ * matmul operand bf16_rne(fp32(q - z) * s), W4_DT_F32 writes fp32(q - z) * s.
+ * Bit-exact with the definition above.  out must be 16-byte aligned.  Source:
+ * the dequantize() reference path of "Re-write HQQ Fused Gemm Transpose". */
+int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                  const w4_desc* desc, void* out, int out_dtype, void* stream);
+
+/* W4A16 matmul on the packed weight of `desc`, fp32 accumulation, fp32 output.
+ *   transposed == 0: Y[m][n] = sum_k A[m][k] * w[n][k] (+ bias[n]),  A = X  [M][K]
+ *   transposed != 0: Y[m][k] = sum_n A[m][n] * w[n][k] (+ bias[k]),  A = dY [M][N]
+ * where w[n][k] = bf16_rne((q - z) * s).  The transposed mode reads the same
+ * packed, scales and zeros buffers.  M == 0 is a no-op.  K % 32 == 0 is
+ * required (W4_ERR_UNSUPPORTED otherwise).  A and packed must be 16-byte
+ * aligned, Y and bias 4-byte aligned.  M <= 4 non-transposed runs the
+ * memory-bound GEMV (no matrix cores); other shapes run the MFMA GEMM.  ws may
+ * be NULL when w4_workspace_bytes reports 0.  Sources: Objective 2 of
+ * "Quantized LLM Inference with Triton Kernels"; "Re-write HQQ Fused Gemm
+ * Transpose"; "[Kernel] Adding bias epilogue support for cutlass_scaled_mm";
+ * "Modify small-batched weight only quantization". */
+int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
+             const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias,
+             float* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* Name of the kernel w4a16_mm would launch for these arguments ("gemv_m4",
+ * "gemm_nt_256x128", ...), or NULL when they are invalid.  Host only. */
+const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed);
+
+/* Human-readable name of a status code. */
+const char* w4_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* w4_last_error(void);
+
+/* Library version string. */
+const char* w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

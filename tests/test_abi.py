@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host-only entry points and argument validation behave
+as documented (no call here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_int4_quantize_amd as w4
+from gemv_int4_quantize_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "w4a16.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(w4\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = w4.lib()
+    names = _declared()
+    assert len(names) >= 9
+    assert sorted(_lib.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert _lib.lib().w4_version().decode().startswith("w4a16-gfx950")
+    for code, name in [(0, "W4_OK"), (-1, "W4_ERR_INVALID"), (-2, "W4_ERR_UNSUPPORTED"), (-3, "W4_ERR_ALIGN"),
+                       (-4, "W4_ERR_RESOURCE"), (-5, "W4_ERR_LAUNCH")]:
+        assert _lib.status_string(code) == name
+
+
+def _pairs(N, K, mode, g=0):
+    out = ctypes.c_int64(-1)
+    st = _lib.lib().w4_meta_pairs(ctypes.byref(_lib.W4Desc(N, K, mode, g)), ctypes.byref(out))
+    return st, out.value
+
+
+def test_meta_pairs():
+    assert _pairs(128256, 2048, _lib.MODE_GLOBAL) == (0, 1)
+    assert _pairs(128256, 2048, _lib.MODE_ROWWISE) == (0, 128256)
+    assert _pairs(128256, 2048, _lib.MODE_GROUPWISE, 16) == (0, 128256 * 128)
+    assert _pairs(4096, 11008, _lib.MODE_GROUPWISE, 64) == (0, 4096 * 172)
+
+
+@pytest.mark.parametrize("N,K,mode,g,why", [
+    (0, 64, 1, 0, "N = 0"),
+    (4, 12, 1, 0, "K not a multiple of 8"),
+    (4, 64, 2, 24, "group not a power of two"),
+    (4, 64, 2, 8, "group below 16"),
+    (4, 64, 2, 128, "group larger than K"),
+    (4, 96, 2, 64, "group does not divide K"),
+    (4, 8192, 2, 8192, "group above 4096"),
+    (4, 64, 7, 0, "unknown mode"),
+])
+def test_invalid_descriptors(N, K, mode, g, why):
+    st, _ = _pairs(N, K, mode, g)
+    assert st == _lib.W4_ERR_INVALID, why
+    assert _lib.last_error()
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    b = ctypes.c_size_t(123)
+    d = _lib.W4Desc(1024, 2048, _lib.MODE_GLOBAL, 0)
+    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_QUANTIZE, 0, ctypes.byref(b)) == 0 and b.value > 0
+    d = _lib.W4Desc(1024, 2048, _lib.MODE_GROUPWISE, 128)
+    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_QUANTIZE, 0, ctypes.byref(b)) == 0 and b.value == 0
+    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM, 4, ctypes.byref(b)) == 0 and b.value == 0
+    assert L.w4_workspace_bytes(ctypes.byref(d), 99, 4, ctypes.byref(b)) == _lib.W4_ERR_INVALID
+
+
+def _mm(A, M, packed, s, z, desc, transposed=0, bias=None, Y=1024):
+    return _lib.lib().w4a16_mm(A, M, packed, s, z, ctypes.byref(desc), transposed, bias, Y, None, 0, None)
+
+
+def test_mm_validation_before_launch():
+    d = _lib.W4Desc(64, 128, _lib.MODE_GROUPWISE, 32)
+    a16 = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+    assert _mm(None, 4, a16, a16, a16, d) == _lib.W4_ERR_INVALID
+    assert _mm(a16, -1, a16, a16, a16, d) == _lib.W4_ERR_INVALID
+    assert _mm(ctypes.c_void_p(0x10008), 4, a16, a16, a16, d) == _lib.W4_ERR_ALIGN
+    assert _mm(a16, 4, ctypes.c_void_p(0x10004), a16, a16, d) == _lib.W4_ERR_ALIGN
+    assert _mm(a16, 4, a16, ctypes.c_void_p(0x10001), a16, d) == _lib.W4_ERR_ALIGN
+    assert _mm(a16, 4, a16, a16, a16, d, Y=ctypes.c_void_p(0x10002)) == _lib.W4_ERR_ALIGN
+    d40 = _lib.W4Desc(64, 40, _lib.MODE_ROWWISE, 0)
+    assert _mm(a16, 4, a16, a16, a16, d40) == _lib.W4_ERR_UNSUPPORTED
+    dn = _lib.W4Desc(60, 128, _lib.MODE_ROWWISE, 0)
+    assert _mm(a16, 4, a16, a16, a16, dn, transposed=1) == _lib.W4_ERR_UNSUPPORTED
+    # M == 0 is a successful no-op and never touches the pointers
+    assert _mm(a16, 0, a16, a16, a16, d) == _lib.W4_OK
+
+
+def test_quantize_validation_before_launch():
+    L = _lib.lib()
+    a16 = ctypes.c_void_p(0x10000)
+    d = _lib.W4Desc(64, 128, _lib.MODE_GROUPWISE, 32)
+    q = L.w4_quantize_pack
+    assert q(a16, 5, ctypes.byref(d), a16, a16, a16, None, 0, None) == _lib.W4_ERR_INVALID
+    assert q(ctypes.c_void_p(0x10008), 1, ctypes.byref(d), a16, a16, a16, None, 0, None) == _lib.W4_ERR_ALIGN
+    dg = _lib.W4Desc(64, 128, _lib.MODE_GLOBAL, 0)
+    assert q(a16, 1, ctypes.byref(dg), a16, a16, a16, None, 0, None) == _lib.W4_ERR_RESOURCE
+    assert q(a16, 1, ctypes.byref(dg), a16, a16, a16, a16, 16, None) == _lib.W4_ERR_RESOURCE
+    dq = L.w4_dequantize
+    assert dq(a16, a16, a16, ctypes.byref(d), a16, _lib.DT_F16, None) == _lib.W4_ERR_INVALID
+    assert dq(a16, a16, a16, ctypes.byref(d), ctypes.c_void_p(0x10004), _lib.DT_BF16, None) == _lib.W4_ERR_ALIGN
+
+
+def test_dispatch_names():
+    # decode shapes go to the GEMV, prefill / fine-tune shapes and the transposed mode to the MFMA GEMM
+    for M in (1, 2, 3, 4):
+        assert w4.kernel_for(M, 4096, 4096, "groupwise", 128) == f"gemv_m{M}"
+    assert w4.kernel_for(5, 4096, 4096, "groupwise", 128).startswith("gemm_nt_")
+    assert w4.kernel_for(2048, 12288, 4096, "rowwise", None).startswith("gemm_nt_")
+    assert w4.kernel_for(2048, 12288, 4096, "groupwise", 64, transposed=True).startswith("gemm_t_")
+    assert w4.kernel_for(4, 4096, 4096, "groupwise", 128, transposed=True).startswith("gemm_t_")
+    assert w4.kernel_for(4, 4096, 40, "rowwise", None) is None

@@ -1,0 +1,220 @@
+"""GPU parity of the W4A16 matmul (GEMV and MFMA GEMM, both directions) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_int4_quantize_amd as w4
+import oracle as O
+import synth
+from gpu_helpers import DEV, assert_mm_close, dev_bf16, dev_f32, dev_weight, host, oracle_rows_global
+
+pytestmark = pytest.mark.gpu
+
+OMODE = {"global": O.GLOBAL, "rowwise": O.ROWWISE, "groupwise": O.GROUPWISE}
+
+
+def _setup(cfg, idx, N, K, mode, g, wdtype="bf16"):
+    w = synth.weight(cfg, idx, N, K, wdtype)
+    w32 = O.to_f32(w, wdtype)
+    ref = O.quantize_pack(w32, OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, wdtype), mode, g)
+    return w32, ref, qw
+
+
+# ------------------------------------------------------------------ small shapes, every mode
+
+
+SMALL_MODES = [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 32), ("groupwise", 64),
+               ("groupwise", 128), ("groupwise", 2048)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("mode,g", SMALL_MODES, ids=[f"{m}{g or ''}" for m, g in SMALL_MODES])
+@pytest.mark.parametrize("N,K", [(37, 2048), (300, 4096), (64, 11008)])
+def test_gemv_small(M, mode, g, N, K):
+    if g is not None and K % g:
+        pytest.skip("group does not divide K")
+    print(f"[case] gemv M={M} N={N} K={K} mode={mode} g={g}", flush=True)
+    _, ref, qw = _setup(700, N + K, N, K, mode, g)
+    x = synth.activations_bf16(700, N + K, M, K)
+    bias = synth.bias_f32(700, N + K, N) if M % 2 else None
+    assert w4.kernel_for(M, N, K, mode, g) == f"gemv_m{M}"
+    y = w4.mm(dev_bf16(x), qw, bias=None if bias is None else dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(x, *ref, K, bias=bias), f"gemv M={M} {mode}{g}")
+
+
+GEMM_MODES = [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 64), ("groupwise", 256)]
+
+
+@pytest.mark.parametrize("M", [5, 17, 128, 129, 300])
+@pytest.mark.parametrize("mode,g", GEMM_MODES, ids=[f"{m}{g or ''}" for m, g in GEMM_MODES])
+@pytest.mark.parametrize("transposed", [False, True], ids=["nt", "t"])
+def test_gemm_small(M, mode, g, transposed):
+    N, K = 264, 1024  # ragged against every tile size in both directions
+    print(f"[case] gemm M={M} N={N} K={K} mode={mode} g={g} t={transposed}", flush=True)
+    _, ref, qw = _setup(701, M, N, K, mode, g)
+    a = synth.activations_bf16(701, M, M, N if transposed else K)
+    bias = synth.bias_f32(701, M, K if transposed else N)
+    y = w4.mm(dev_bf16(a), qw, transposed=transposed, bias=dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(a, *ref, K, transposed, bias), f"gemm M={M} {mode}{g} t={transposed}")
+
+
+@pytest.mark.parametrize("M", [2, 8, 200])
+@pytest.mark.parametrize("transposed", [False, True], ids=["nt", "t"])
+def test_onehot_exact(M, transposed):
+    """A one-hot activation row selects one dequantized weight row or column exactly (bit-exact)."""
+    N, K = 136, 512
+    _, ref, qw = _setup(702, M, N, K, "groupwise", 32)
+    wd = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref, K))
+    L = N if transposed else K
+    a = np.zeros((M, L), dtype=np.uint16)
+    hot = [(m * 37 + 5) % L for m in range(M)]
+    for m in range(M):
+        a[m, hot[m]] = 0x3F80
+    y = host(w4.mm(dev_bf16(a), qw, transposed=transposed)).astype(np.float64)
+    for m in range(M):
+        want = wd[hot[m], :] if transposed else wd[:, hot[m]]
+        np.testing.assert_array_equal(y[m], want)
+
+
+def test_single_matmul_case():
+    """X bf16 [4][2048], W fp32 [2048][2048] ~ N(0, 0.02), groupwise g=128, seed 0."""
+    x, w = synth.single_matmul_case()
+    ref = O.quantize_pack(w, O.GROUPWISE, 128)
+    qw = w4.quantize_pack(dev_weight(w, "f32"), "groupwise", 128)
+    y = w4.mm(dev_bf16(x), qw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(qw.packed), ref[0])
+    assert_mm_close(host(y), O.matmul(x, *ref, 2048), "single matmul")
+
+
+def test_deterministic_and_empty():
+    N, K = 512, 2048
+    _, ref, qw = _setup(703, 0, N, K, "groupwise", 128)
+    for M, t in [(3, False), (256, False), (256, True)]:
+        a = dev_bf16(synth.activations_bf16(703, M, M, N if t else K))
+        y1 = w4.mm(a, qw, transposed=t)
+        y2 = w4.mm(a, qw, transposed=t)
+        assert torch.equal(y1, y2)
+    e = w4.mm(torch.empty((0, K), dtype=torch.bfloat16, device=DEV), qw)
+    assert e.shape == (0, N)
+
+
+def test_bias_on_minus_off():
+    N, K, M = 384, 2048, 130
+    _, ref, qw = _setup(704, 0, N, K, "rowwise", None)
+    x = dev_bf16(synth.activations_bf16(704, 1, M, K))
+    b = synth.bias_f32(704, 2, N)
+    d = host(w4.mm(x, qw, bias=dev_f32(b))).astype(np.float64) - host(w4.mm(x, qw)).astype(np.float64)
+    assert np.allclose(d, np.broadcast_to(b.astype(np.float64), d.shape), rtol=0, atol=2e-6)
+
+
+def test_fused_qkv_equivalence():
+    """One fused QKV operand equals separate Q, K, V in both directions."""
+    K = 1024
+    sizes = (512, 256, 256)
+    ws = [synth.weight(705, i, n, K, "bf16", tensor_id=synth.T_Q + i) for i, n in enumerate(sizes)]
+    for mode, g in [("rowwise", None), ("groupwise", 64)]:
+        fused = w4.quantize_fused([dev_weight(w, "bf16") for w in ws], mode, g)
+        parts = [w4.quantize_pack(dev_weight(w, "bf16"), mode, g) for w in ws]
+        for M in (4, 256):
+            x = dev_bf16(synth.activations_bf16(705, M, M, K))
+            yf = host(w4.mm(x, fused))
+            ys = np.concatenate([host(w4.mm(x, p)) for p in parts], axis=1)
+            assert_mm_close(yf, ys, f"fused NT {mode} M={M}")
+            dy = synth.activations_bf16(705, M + 1, M, sum(sizes))
+            dxf = host(w4.mm(dev_bf16(dy), fused, transposed=True))
+            offs = np.cumsum((0,) + sizes)
+            dxs = sum(host(w4.mm(dev_bf16(np.ascontiguousarray(dy[:, offs[i]:offs[i + 1]])), parts[i],
+                                 transposed=True)).astype(np.float64) for i in range(3))
+            assert_mm_close(dxf, dxs, f"fused T {mode} M={M}")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled outputs
+
+DECODE_SHAPES = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (2048, 2048), (8192, 8192),
+                 (16384, 16384)]
+
+
+@pytest.mark.parametrize("si", range(len(DECODE_SHAPES)), ids=[f"{n}x{k}" for n, k in DECODE_SHAPES])
+def test_decode_gemv_full(si):
+    """Decode batched GEMV, Llama-2-7B-like layers, g=128, M = 1..4: sampled rows of Y."""
+    N, K = DECODE_SHAPES[si]
+    print(f"[case] decode full N={N} K={K}", flush=True)
+    w = synth.weight(2, si, N, K, "bf16")
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), "groupwise", 128)
+    rows = np.sort(np.random.default_rng(si).choice(N, 48, replace=False))
+    ref = O.quantize_pack(O.to_f32(w[rows], "bf16"), O.GROUPWISE, 128)
+    for M in (1, 2, 3, 4):
+        x = synth.activations_bf16(2, si * 10 + M, M, K)
+        y = host(w4.mm(dev_bf16(x), qw))
+        assert_mm_close(y[:, rows], O.matmul(x, *ref, K), f"decode {N}x{K} M={M}")
+
+
+PREFILL_SHAPES = [(2048, 2048), (8192, 2048), (2048, 8192), (512, 2048), (128256, 2048)]
+
+
+@pytest.mark.parametrize("si", range(len(PREFILL_SHAPES)), ids=[f"{n}x{k}" for n, k in PREFILL_SHAPES])
+def test_prefill_gemm_full(si):
+    """Prefill GEMM, Llama-3.2-1B-like shapes, M in {128, 512, 2048}, three modes, fp32 bias: sampled outputs."""
+    N, K = PREFILL_SHAPES[si]
+    w = synth.weight(3, si, N, K, "bf16")
+    w32 = O.to_f32(w, "bf16")
+    wd = dev_weight(w, "bf16")
+    bias = synth.bias_f32(3, si, N)
+    rows = np.sort(np.random.default_rng(100 + si).choice(N, min(N, 40), replace=False))
+    for mode, g in [("global", None), ("rowwise", None), ("groupwise", 64)]:
+        print(f"[case] prefill full N={N} K={K} mode={mode}", flush=True)
+        qw = w4.quantize_pack(wd, mode, g)
+        if mode == "global":
+            ref = oracle_rows_global(w32, rows)
+        else:
+            ref = O.quantize_pack(w32[rows], OMODE[mode], g)
+        for M in (128, 512, 2048):
+            x = synth.activations_bf16(3, si * 10 + M, M, K)
+            y = w4.mm(dev_bf16(x), qw, bias=dev_f32(bias))
+            ms = np.sort(np.random.default_rng(M).choice(M, 24, replace=False))
+            ys = host(y[torch.from_numpy(ms).to(DEV)][:, torch.from_numpy(rows).to(DEV)])
+            del y
+            assert_mm_close(ys, O.matmul(x[ms], *ref, K, bias=bias[rows]), f"prefill {N}x{K} {mode} M={M}")
+
+
+QLORA_SHAPES = [(12288, 4096), (11008, 4096), (4096, 11008)]
+
+
+@pytest.mark.parametrize("si", range(len(QLORA_SHAPES)), ids=[f"{n}x{k}" for n, k in QLORA_SHAPES])
+def test_qlora_pair_full(si):
+    """QLoRA pair on one packed buffer: Y = X w^T and dX = dY w, rowwise and g=64: sampled outputs."""
+    N, K = QLORA_SHAPES[si]
+    if si == 0:  # fused QKV packed from separate Q, K, V
+        ws = [synth.weight(4, 0, 4096, K, "bf16", tensor_id=synth.T_Q + i) for i in range(3)]
+        w = np.concatenate(ws, axis=0)
+    else:
+        ws = None
+        w = synth.weight(4, si, N, K, "bf16")
+    w32 = O.to_f32(w, "bf16")
+    for mode, g in [("rowwise", None), ("groupwise", 64)]:
+        print(f"[case] qlora full N={N} K={K} mode={mode}", flush=True)
+        if ws is not None:
+            qw = w4.quantize_fused([dev_weight(p, "bf16") for p in ws], mode, g)
+        else:
+            qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
+        ref_full = O.quantize_pack(w32, OMODE[mode], g)
+        wdq = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref_full, K))  # oracle weight operand [N][K]
+        rows = np.sort(np.random.default_rng(200 + si).choice(N, 32, replace=False))
+        for M in (1024, 2048, 4096):
+            ms = np.sort(np.random.default_rng(M + si).choice(M, 12, replace=False))
+            msd = torch.from_numpy(ms).to(DEV)
+            x = synth.activations_bf16(4, si * 10 + M, M, K)
+            y = w4.mm(dev_bf16(x), qw)
+            ys = host(y[msd][:, torch.from_numpy(rows).to(DEV)])
+            del y
+            yref = O.bf16_bits_to_f64(x[ms]) @ wdq[rows].T
+            assert_mm_close(ys, yref, f"qlora NT {N}x{K} {mode} M={M}")
+            dy = synth.activations_bf16(4, si * 10 + M, M, N, tensor_id=synth.T_DY)
+            dx = w4.mm(dev_bf16(dy), qw, transposed=True)
+            dxs = host(dx[msd])
+            del dx
+            dxref = O.bf16_bits_to_f64(dy[ms]) @ wdq
+            assert_mm_close(dxs, dxref, f"qlora T {N}x{K} {mode} M={M}")

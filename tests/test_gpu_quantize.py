@@ -1,0 +1,132 @@
+"""GPU parity of quantize-and-pack and dequantize: bit-exact with the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_int4_quantize_amd as w4
+import oracle as O
+import synth
+from gpu_helpers import (DEV, assert_quant_equal, dev_weight, host, host_bits16, oracle_rows_global)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 32), ("groupwise", 64),
+         ("groupwise", 128), ("groupwise", 256), ("groupwise", 512), ("groupwise", 1024), ("groupwise", 4096)]
+OMODE = {"global": O.GLOBAL, "rowwise": O.ROWWISE, "groupwise": O.GROUPWISE}
+
+
+def _special_weight(N, K, seed):
+    r = np.random.default_rng(seed)
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[0, :] = 0.0                       # all-zero row
+    w[1, : K // 2] = 0.75               # constant half row
+    w[2, :] = np.abs(w[2, :]) + 0.1     # all positive
+    w[3, :] = -np.abs(w[3, :]) - 0.1    # all negative
+    w[4, 5] = 3.0                       # outliers
+    w[5, 17] = -2.5
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode,g", MODES, ids=[f"{m}{g or ''}" for m, g in MODES])
+def test_quantize_bit_exact_small(dtype, mode, g):
+    print(f"[case] quantize small dtype={dtype} mode={mode} g={g}", flush=True)
+    N, K = 37, 4096          # ragged N, several groups per row for every g
+    w = _special_weight(N, K, 10)
+    if dtype == "f16":
+        w = w.astype(np.float16)
+    elif dtype == "bf16":
+        w = synth.f32_to_bf16_bits(w)
+    w32 = O.to_f32(w, dtype)
+    ref = O.quantize_pack(w32, OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, dtype), mode, g)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"{dtype} {mode} {g}")
+
+
+@pytest.mark.parametrize("N,K,mode,g", [(1, 8, "rowwise", None), (3, 24, "rowwise", None), (5, 1376, "rowwise", None),
+                                        (2, 11008, "rowwise", None), (4, 16384, "rowwise", None),
+                                        (7, 48, "groupwise", 16), (1, 4096, "groupwise", 4096),
+                                        (9, 2056, "global", None)])
+def test_quantize_odd_shapes(N, K, mode, g):
+    print(f"[case] quantize odd N={N} K={K} mode={mode} g={g}", flush=True)
+    w = synth.weight(500, N * 7 + K, N, K, "f16")
+    w32 = O.to_f32(w, "f16")
+    ref = O.quantize_pack(w32, OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "f16"), mode, g)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"N={N} K={K} {mode} {g}")
+
+
+@pytest.mark.parametrize("mode,g", [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 32),
+                                    ("groupwise", 64), ("groupwise", 128), ("groupwise", 256), ("groupwise", 512),
+                                    ("groupwise", 1024), ("groupwise", 2048)])
+def test_quantize_full_size_sampled(mode, g, full_quant_weight):
+    """fp16 W [128256][2048] with 0.1% outliers: every scale / zero and sampled rows of codes."""
+    print(f"[case] quantize full 128256x2048 mode={mode} g={g}", flush=True)
+    w, wd, rows = full_quant_weight
+    w32 = O.to_f32(w[rows], "f16")
+    qw = w4.quantize_pack(wd, mode, g)
+    torch.cuda.synchronize()
+    if mode == "global":
+        ref = oracle_rows_global(O.to_f32(w, "f16"), rows)
+    else:
+        ref = O.quantize_pack(w32, OMODE[mode], g)
+    assert_quant_equal(qw, *ref, rows=rows, what=f"full {mode} {g}")
+
+
+@pytest.fixture(scope="module")
+def full_quant_weight():
+    N, K = 128256, 2048
+    w = synth.weight_with_outliers(5, 0, N, K)
+    rows = np.sort(np.random.default_rng(55).choice(N, 96, replace=False))
+    rows = np.concatenate([[0, N - 1], rows])
+    wd = dev_weight(w, "f16")
+    yield w, wd, rows
+    del wd
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode,g", [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 128),
+                                    ("groupwise", 2048)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_dequantize_bit_exact(mode, g, out):
+    print(f"[case] dequantize mode={mode} g={g} out={out}", flush=True)
+    N, K = 33, 2048
+    w = _special_weight(N, K, 11)
+    p, s, z = O.quantize_pack(w, OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "f32"), mode, g)
+    if out == "bf16":
+        d = w4.dequantize(qw, torch.bfloat16)
+        np.testing.assert_array_equal(host_bits16(d), O.dequantize_bf16_bits(p, s, z, K))
+    else:
+        d = w4.dequantize(qw, torch.float32)
+        np.testing.assert_array_equal(host(d).view(np.uint32), O.dequantize_f32(p, s, z, K).view(np.uint32))
+
+
+def test_dequantize_tiny_zero_order():
+    """Zeros so small that q - z is inexact in fp32: the export keeps subtract-then-multiply."""
+    N, K = 4, 64
+    q = np.tile(np.arange(16, dtype=np.uint8), (N, K // 16))
+    p = O.pack(q)
+    s = np.array([[0.0276336669921875], [0.0026454925537109375], [0.04571533203125], [0.5]], dtype=np.float16)
+    z = np.array([[0.00046753883361816406], [-0.0003650188446044922], [0.0003650188446044922], [3.0]],
+                 dtype=np.float16)
+    qw = w4.QuantizedWeight(packed=torch.from_numpy(p).to(DEV), scales=torch.from_numpy(s).to(DEV),
+                            zeros=torch.from_numpy(z).to(DEV), N=N, K=K, mode=1, group=0)
+    d = w4.dequantize(qw, torch.float32)
+    np.testing.assert_array_equal(host(d).view(np.uint32), O.dequantize_f32(p, s, z, K).view(np.uint32))
+
+
+def test_quantize_into_row_slices_matches_separate():
+    """Fused-QKV construction: quantizing Q, K, V into one operand equals the oracle's row concatenation."""
+    K = 1024
+    parts = [synth.weight(6, i, n, K, "bf16", tensor_id=synth.T_Q + i) for i, n in enumerate((256, 128, 128))]
+    for mode, g in [("rowwise", None), ("groupwise", 64)]:
+        ref = O.fuse_rows([O.quantize_pack(O.to_f32(p, "bf16"), OMODE[mode], g) for p in parts])
+        qw = w4.quantize_fused([dev_weight(p, "bf16") for p in parts], mode, g)
+        torch.cuda.synchronize()
+        assert_quant_equal(qw, *ref, what=f"fused {mode}")
+    with pytest.raises(ValueError):
+        w4.quantize_fused([dev_weight(p, "bf16") for p in parts], "global", None)
