@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+Headline workload (one "step"): the decode batched GEMV sweep at Llama-2-7B-like
+layer shapes, groupwise g=128 along K, M in {1, 2, 3, 4}; (N, K) in
+{(12288,4096) fused QKV, (4096,4096) o_proj, (22016,4096) fused gate+up,
+(4096,11008) down, (2048,2048), (8192,8192), (16384,16384)}; X bf16 ~ N(0,1),
+W ~ N(0,0.02) quantized on the GPU before timing.  28 launches per step.
+
+value = algorithmic bytes of a step / GPU time of a step (GB/s), where a launch
+moves N*K/2 (codes) + 4*N*K/g (fp16 scale + zero) + 2*M*K (X) + 4*M*N (Y) bytes.
+Weights rotate through >= 1 GiB of distinct copies so no launch finds its
+weights in the 256 MB Infinity Cache.
+
+Also reported in the same JSON line (context, not `value`):
+  gemm      QLoRA pair at Llama-2-7B layer shapes: M in {1024, 2048, 4096},
+            (N,K) in {(12288,4096) fused QKV, (11008,4096), (4096,11008)}, rowwise
+            and g=64, forward Y = X w^T and transposed dX = dY w on one packed buffer;
+            TFLOP/s = 2MNK / kernel time, fraction of the 2.5 PFLOP/s bf16 peak.
+  quantize  fp16 W [128256][2048] ~ N(0,0.02) with 0.1% outliers ~ N(0,0.5), ten
+            modes: packed GB/s, MAE of the fp32 dequantization, compression ratio.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the GEMV sweep.
+
+Timing: the GPU is parked on a spin kernel while the host enqueues the whole
+batch, so the two HIP events around it measure back-to-back GPU execution, not
+host overhead.  The timed region is `steps` steps of the sweep; per-shape figures
+come from separate batches of 20 launches of one shape.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+DECODE_SHAPES = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (2048, 2048), (8192, 8192),
+                 (16384, 16384)]
+DECODE_G = 128
+QLORA_SHAPES = [(12288, 4096), (11008, 4096), (4096, 11008)]
+QLORA_M = [1024, 2048, 4096]
+QUANT_MODES = [("global", None), ("rowwise", None)] + [("groupwise", g) for g in (16, 32, 64, 128, 256, 512, 1024,
+                                                                                   2048)]
+POOL_BYTES = 1 << 30
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(M: int, N: int, K: int, g: int) -> int:
+    return N * K // 2 + 4 * N * (K // g) + 2 * M * K + 4 * M * N
+
+
+def source_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gemv_int4_quantize_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def run_batch(torch, fns, spin_cycles: int | None = None) -> float:
+    """Run `fns` back-to-back behind a GPU spin (so the host enqueues ahead of the GPU);
+    returns the GPU time in ms from the first to the last launch (two events)."""
+    torch.cuda.synchronize()
+    if spin_cycles is None:
+        spin_cycles = int(2.4e9 * 100e-6 * len(fns)) + 2_000_000
+    torch.cuda._sleep(spin_cycles)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for fn in fns:
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def clone_qw(w4, qw):
+    return w4.QuantizedWeight(qw.packed.clone(), qw.scales.clone(), qw.zeros.clone(), qw.N, qw.K, qw.mode, qw.group)
+
+
+def dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def bench_gemv(torch, w4, synth, args):
+    """The headline sweep: returns (result dict, per-launch records)."""
+    import numpy as np
+    per_copy = sum(N * K // 2 + 4 * N * (K // DECODE_G) for N, K in DECODE_SHAPES)
+    copies = max(4, math.ceil(POOL_BYTES / per_copy))
+    log(f"GEMV sweep: {len(DECODE_SHAPES)} shapes x M=1..4, pool of {copies} weight copies "
+        f"({copies * per_copy / 2**30:.2f} GiB)")
+    layers = []
+    for si, (N, K) in enumerate(DECODE_SHAPES):
+        w = synth.weight(2, si, N, K, "bf16")
+        qw = w4.quantize_pack(dev_bf16(torch, w), "groupwise", DECODE_G)
+        del w
+        pool = [qw] + [clone_qw(w4, qw) for _ in range(copies - 1)]
+        xs = {M: dev_bf16(torch, synth.activations_bf16(2, si * 10 + M, M, K)) for M in (1, 2, 3, 4)}
+        ys = {M: torch.empty((M, N), dtype=torch.float32, device="cuda") for M in (1, 2, 3, 4)}
+        layers.append((N, K, pool, xs, ys))
+    torch.cuda.synchronize()
+
+    launches = []   # (M, N, K) in step order
+    for (N, K, pool, xs, ys) in layers:
+        for M in (1, 2, 3, 4):
+            launches.append((M, N, K))
+    step_bytes = sum(gemv_bytes(M, N, K, DECODE_G) for M, N, K in launches)
+
+    counter = [0]
+
+    def make_step():
+        fns = []
+        for (N, K, pool, xs, ys) in layers:
+            for M in (1, 2, 3, 4):
+                def fn(N=N, K=K, pool=pool, x=xs[M], y=ys[M]):
+                    qw = pool[counter[0] % len(pool)]
+                    counter[0] += 1
+                    w4.mm(x, qw, out=y)
+                fns.append(fn)
+        return fns
+
+    for _ in range(args.warmup):
+        run_batch(torch, make_step())
+    fns = []
+    for _ in range(args.steps):
+        fns += make_step()
+    span = run_batch(torch, fns)  # the timed region: `steps` steps, launches back-to-back
+    n = len(launches)
+    ms_per_step = span / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # per-shape figures: 20 back-to-back launches of one point, rotating weight copies
+    points = []
+    point_ms = []
+    for (N, K, pool, xs, ys) in layers:
+        for M in (1, 2, 3, 4):
+            batch = [lambda qw=pool[i % len(pool)], x=xs[M], y=ys[M]: w4.mm(x, qw, out=y) for i in range(20)]
+            t = run_batch(torch, batch) / len(batch)
+            point_ms.append(t)
+            b = gemv_bytes(M, N, K, DECODE_G)
+            points.append({"M": M, "N": N, "K": K, "us": round(t * 1e3, 3), "GBps": round(b / (t * 1e-3) / 1e9, 1),
+                           "kernel": w4.kernel_for(M, N, K, "groupwise", DECODE_G)})
+    kernel_time_s = sum(point_ms) * 1e-3
+    achieved = step_bytes / kernel_time_s / 1e9
+    return {
+        "value": value, "ms_per_step": ms_per_step, "step_bytes": step_bytes, "achieved_gbs": achieved,
+        "mean_launch_us": ms_per_step * 1e3 / n, "launches_per_step": n, "points": points,
+        "pool_copies": copies,
+    }
+
+
+def bench_gemm(torch, w4, synth, reps: int):
+    import numpy as np
+    log("QLoRA GEMM pair: 3 shapes x {rowwise, g64} x M in {1024, 2048, 4096} x {NT, T}")
+    pts = []
+    for si, (N, K) in enumerate(QLORA_SHAPES):
+        if si == 0:
+            parts = [dev_bf16(torch, synth.weight(4, 0, 4096, K, "bf16", tensor_id=synth.T_Q + i)) for i in range(3)]
+        else:
+            parts = None
+            wd = dev_bf16(torch, synth.weight(4, si, N, K, "bf16"))
+        for mode, g in [("rowwise", None), ("groupwise", 64)]:
+            qw = w4.quantize_fused(parts, mode, g) if parts is not None else w4.quantize_pack(wd, mode, g)
+            for M in QLORA_M:
+                x = dev_bf16(torch, synth.activations_bf16(4, si * 10 + M, M, K))
+                dy = dev_bf16(torch, synth.activations_bf16(4, si * 10 + M, M, N, tensor_id=synth.T_DY))
+                y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                dx = torch.empty((M, K), dtype=torch.float32, device="cuda")
+                run_batch(torch, [lambda: w4.mm(x, qw, out=y), lambda: w4.mm(dy, qw, transposed=True, out=dx)])
+                t_nt = run_batch(torch, [lambda: w4.mm(x, qw, out=y)] * reps) / reps * 1e-3
+                t_t = run_batch(torch, [lambda: w4.mm(dy, qw, transposed=True, out=dx)] * reps) / reps * 1e-3
+                fl = 2.0 * M * N * K
+                pts.append({"M": M, "N": N, "K": K, "mode": mode if g is None else f"g{g}",
+                            "nt_tflops": round(fl / t_nt / 1e12, 1), "t_tflops": round(fl / t_t / 1e12, 1),
+                            "t_over_nt": round(t_t / t_nt, 3), "nt_us": round(t_nt * 1e6, 1),
+                            "t_us": round(t_t * 1e6, 1),
+                            "nt_kernel": w4.kernel_for(M, N, K, mode, g), "t_kernel": w4.kernel_for(M, N, K, mode, g,
+                                                                                                   True)})
+                del x, dy, y, dx
+            del qw
+        torch.cuda.empty_cache()
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
+    t_nt = sum(p["nt_us"] for p in pts) * 1e-6
+    t_t = sum(p["t_us"] for p in pts) * 1e-6
+    big = [p for p in pts if p["M"] >= 512]
+    return {
+        "workload": "QLoRA pair, Llama-2-7B layer shapes, one packed buffer per weight",
+        "nt_tflops": round(fl / t_nt / 1e12, 1), "t_tflops": round(fl / t_t / 1e12, 1),
+        "nt_frac_of_peak": round(fl / t_nt / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "t_frac_of_peak": round(fl / t_t / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "t_over_nt_total": round(t_t / t_nt, 3),
+        "t_over_nt_max": max(p["t_over_nt"] for p in pts),
+        "min_tflops_m_ge_512": min(min(p["nt_tflops"], p["t_tflops"]) for p in big),
+        "points": pts,
+    }
+
+
+def bench_quantize(torch, w4, synth, reps: int):
+    import numpy as np
+    N, K = 128256, 2048
+    log(f"quantize-pack: fp16 [{N}][{K}] with 0.1% outliers, {len(QUANT_MODES)} modes")
+    wd = torch.from_numpy(synth.weight_with_outliers(5, 0, N, K)).cuda()
+    w64 = None
+    out = []
+    for mode, g in QUANT_MODES:
+        qw = w4.quantize_pack(wd, mode, g)
+        t = run_batch(torch, [lambda: w4.quantize_pack(wd, mode, g)] * reps) / reps * 1e-3
+        pairs = 1 if mode == "global" else (N if mode == "rowwise" else N * K // g)
+        reads = 2 if mode == "global" else 1
+        nbytes = reads * N * K * 2 + N * K // 2 + 4 * pairs
+        deq = w4.dequantize(qw, torch.float32)
+        if w64 is None:
+            w64 = wd.to(torch.float64)
+        mae = float((deq.to(torch.float64) - w64).abs().mean())
+        del deq
+        comp = (N * K * 2.0) / (N * K / 2.0 + 4.0 * pairs)
+        out.append({"mode": mode if g is None else f"g{g}", "us": round(t * 1e6, 1),
+                    "GBps": round(nbytes / t / 1e9, 1), "frac_of_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "mae": round(mae, 6), "compression": round(comp, 6)})
+    del wd, w64
+    torch.cuda.empty_cache()
+    return {"workload": "fp16 W [128256][2048] ~ N(0,0.02) + 0.1% N(0,0.5) outliers", "points": out}
+
+
+def cpu_baseline(synth, budget_s: float):
+    """The CPU oracle on a bounded sample of the GEMV sweep (algorithmic GB/s)."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    # shapes of the sweep in order, every M; stops once the budget of oracle time is spent
+    sample = [(si, M) for si in (1, 0, 3, 2, 5) for M in (1, 2, 3, 4)]
+    done, total_bytes, t_total = [], 0, 0.0
+    cache = {}
+    for si, M in sample:
+        N, K = DECODE_SHAPES[si]
+        if si not in cache:
+            cache.clear()
+            w = synth.weight(2, si, N, K, "bf16")
+            cache[si] = O.quantize_pack(O.to_f32(w, "bf16"), O.GROUPWISE, DECODE_G)
+            del w
+        p, s, z = cache[si]
+        x = synth.activations_bf16(2, si * 10 + M, M, K)
+        t0 = time.perf_counter()
+        O.matmul(x, p, s, z, K)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        total_bytes += gemv_bytes(M, N, K, DECODE_G)
+        done.append(f"{N}x{K}/M{M}")
+        if t_total > budget_s:
+            break
+    return {"value": round(total_bytes / t_total / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "oracle matmul (bf16 dequantize + float64 BLAS product) on " + ", ".join(done) +
+                      f" of the decode sweep, {t_total:.1f} s"}
+
+
+def load_traffic(step_bytes_per_launch: float):
+    """HBM traffic per launch from the committed counter summary, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemv_decode_sweep_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except OSError:
+        return None
+    if d.get("source_hash") != source_hash("gemv.hip", "common.h"):
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="skip the GEMM and quantize blocks")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--details", default=None, help="write per-point results (JSON) to this path")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the W4A16 kernels run on a single GPU and this build has no "
+              "multi-GPU path (--gpus must be 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import gemv_int4_quantize_amd as w4
+    import synth
+
+    w4.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    g = bench_gemv(torch, w4, synth, args)
+    log(f"GEMV sweep: {g['value']:.1f} GB/s per step, {g['achieved_gbs']:.1f} GB/s kernel-only")
+    per_launch_bytes = g["step_bytes"] / g["launches_per_step"]
+    traffic = load_traffic(per_launch_bytes)
+    result = {
+        "metric": "W4A16 GEMV GB/s + GEMM TFLOP/s at Llama-7B shapes, % of MI355X roofline",
+        "value": round(g["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(g["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode batched GEMV sweep, Llama-2-7B-like layers, groupwise g=128, M=1..4",
+                   "shapes_NxK": [f"{n}x{k}" for n, k in DECODE_SHAPES], "M": [1, 2, 3, 4], "group": DECODE_G,
+                   "launches_per_step": g["launches_per_step"], "bytes_per_step": g["step_bytes"],
+                   "weight_pool_copies": g["pool_copies"]},
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel (28 launches per step, per-shape batches)",
+                     "achieved": round(g["achieved_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g["achieved_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "mean_launch_us": round(g["mean_launch_us"], 3),
+                     "algorithmic_bytes_per_launch": round(per_launch_bytes, 1)},
+    }
+    details = {"gemv": g["points"]}
+    if not args.no_extras:
+        gm = bench_gemm(torch, w4, synth, reps=5)
+        result["gemm"] = {k: v for k, v in gm.items() if k != "points"}
+        result["gemm"]["roofline"] = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "achieved_nt": gm["nt_tflops"], "achieved_t": gm["t_tflops"],
+                                      "frac_nt": gm["nt_frac_of_peak"], "frac_t": gm["t_frac_of_peak"]}
+        details["gemm"] = gm["points"]
+        log(f"GEMM: NT {gm['nt_tflops']} TFLOP/s, T {gm['t_tflops']} TFLOP/s, T/NT {gm['t_over_nt_total']}")
+        qz = bench_quantize(torch, w4, synth, reps=5)
+        result["quantize"] = {"workload": qz["workload"],
+                              "GBps": {p["mode"]: p["GBps"] for p in qz["points"]},
+                              "mae": {p["mode"]: p["mae"] for p in qz["points"]},
+                              "compression": {p["mode"]: p["compression"] for p in qz["points"]}}
+        details["quantize"] = qz["points"]
+        log("quantize: " + ", ".join(f"{p['mode']} {p['GBps']} GB/s" for p in qz["points"]))
+    if not args.no_cpu:
+        cb = cpu_baseline(synth, args.cpu_budget)
+        result["cpu_baseline"] = cb
+        log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads")
+    else:
+        result["cpu_baseline"] = None
+    if args.details:
+        os.makedirs(os.path.dirname(os.path.abspath(args.details)), exist_ok=True)
+        with open(args.details, "w") as f:
+            json.dump({"result": result, "details": details}, f, indent=1)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -7,11 +7,13 @@
 //   * each wave owns R rows over the full K (split-K inside the wave, no partial
 //     results leave the wave); lane l streams 16-byte chunks c = l, l+64, ... of
 //     every row (32 codes each), so one wave-wide load is 1 KB contiguous;
-//   * X is staged once per workgroup in LDS as 4 planes ([m][word][chunk]) so that
-//     consecutive lanes read consecutive 16-byte slots (no bank conflicts);
-//   * GROUPWISE scale / zero pairs of the 2048 columns one iteration covers are
-//     loaded once per group by the wave and staged in LDS as the fp32 constants of
-//     the in-register dequantization (s*2^24, s*2^20, -z*s);
+//   * X streams through two LDS windows of 2048 columns ([m][word][chunk], so that
+//     consecutive lanes read consecutive 16-byte slots, free of bank conflicts); the
+//     block refills one window while it computes on the other, so the LDS footprint
+//     (8 KB per activation row) does not grow with K;
+//   * the scale / zero bits of a chunk's group are loaded with the chunk, one
+//     iteration ahead (the lanes that share a group issue the same address inside one
+//     wave-wide load, which the memory pipeline merges into one request);
 //   * dequantization is v_fma_mix_f32 on nibbles masked into fp16 halves, bf16
 //     rounding by v_cvt_pk_bf16_f32, products by v_dot2_f32_bf16;
 //   * the R*M partial sums of a wave are reduced with a transposing butterfly, so
@@ -19,13 +21,8 @@
 #include "common.h"
 #include "launch.h"
 
-#include <atomic>
 
 namespace w4 {
-
-struct alignas(16) DqEntry {
-  float s24, s20, nzs, pad;
-};
 
 // Lane l ends up holding the wave-wide sum of value (l >> (6 - log2 V)).
 template <int V>
@@ -52,56 +49,101 @@ __device__ __forceinline__ float transpose_reduce(float (&v)[V], int lane) {
   return v[0];
 }
 
-template <int M, int R, int META, int WAVES>
+// Per-lane state of one pipeline stage: the 16-byte chunk of every row and the
+// raw fp16 scale / zero bits of the group(s) it belongs to (GPC groups per chunk).
+template <int R, int GPC>
+struct Stage {
+  u32x4 w[R];
+  uint16_t s[R][GPC], z[R][GPC];  // kept 16-bit: v_fma_mix_f32 reads the low half as fp16
+};
+
+// Dequantization constants from raw fp16 bits, three v_fma_mix_f32 (exact):
+// s * 2^24, s * 2^20 and -(z * s).
+__device__ __forceinline__ DqConst dq_const_mix(uint16_t s_bits, uint16_t z_bits) {
+  DqConst c;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s24) : "v"(s_bits), "v"(16777216.0f));
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s20) : "v"(s_bits), "v"(1048576.0f));
+  asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(c.nzs) : "v"(z_bits), "v"(s_bits));
+  return c;
+}
+
+// One iteration covers 2048 columns: 64 lanes x one 16-byte chunk (32 codes) per row.
+constexpr int kIterCols = 2048;
+
+template <int M, int R, int META, int WAVES, int GPC>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __restrict__ X,
                                                           const int32_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ zeros,
                                                           const float* __restrict__ bias, float* __restrict__ Y,
-                                                          int N, int K, int g) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int KS = K >> 5;  // 16-byte chunks (32 codes) per row
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+                                                          int N, int K, int log2g) {
+  // Two LDS windows of X, each [m][word][chunk] over the 2048 columns of one iteration:
+  // the block refills one window while it computes on the other.
+  __shared__ u32x4 xwin[2][M * 4 * 64];
+  constexpr int T = WAVES * 64;
+  constexpr int XUNITS = M * 4 * 64;  // 16-byte units per window
+  const int KS = K >> 5;              // 16-byte chunks (32 codes) per row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // the wave index is uniform: keep every row-dependent value in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row0 = (blockIdx.x * WAVES + wave) * R;
   const int iters = (KS + 63) >> 6;
+  const int gpr = META == META_GROUP ? K >> log2g : 1;
+  const int KW = K >> 3;
 
-  // groups covered by one iteration (2048 columns) and the per-wave table
-  const int gpi = META == META_GROUP ? (g >= 2048 ? 1 : 2048 / g) : 1;
-  DqEntry* tbl = reinterpret_cast<DqEntry*>(smem + (size_t)M * K * 2) + (size_t)wave * R * gpi;
-  const int gpr = META == META_GROUP ? K / g : 1;
-
-  int rows[R];
+  const u32x4* prow[R];
+  const uint16_t* srow[R];
+  const uint16_t* zrow[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(row0 + r, N - 1);
-
-  // first packed chunk of every row: in flight while X is staged
-  u32x4 wv[R];
-  {
-    const int c = min(lane, KS - 1);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      wv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + (size_t)rows[r] * (K >> 3)) + c);
+  for (int r = 0; r < R; ++r) {
+    const int n = min(row0 + r, N - 1);
+    prow[r] = reinterpret_cast<const u32x4*>(packed + (size_t)n * KW);
+    srow[r] = scales + (size_t)n * gpr;
+    zrow[r] = zeros + (size_t)n * gpr;
   }
 
-  // stage X in the plane layout
-  for (int u = threadIdx.x; u < M * KS * 4; u += WAVES * 64) {
-    const int m = u / (KS * 4);
-    const int rem = u - m * KS * 4;
-    const int c = rem >> 2, w = rem & 3;
-    xs[(m * 4 + w) * KS + c] = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + c * 32 + w * 8);
-  }
-
-  DqConst rc[R];
-  if constexpr (META != META_GROUP) {
+  // X units this thread moves into a window: unit u = (m * 64 + chunk) * 4 + word
+  constexpr int XPT = (XUNITS + T - 1) / T;
+  u32x4 xr[XPT];
+  auto xload = [&](int it) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int mi = META == META_GLOBAL ? 0 : rows[r];
-      rc[r] = dq_const(scales[mi], zeros[mi]);
+    for (int i = 0; i < XPT; ++i) {
+      const int u = tid + i * T;
+      if (u < XUNITS) {
+        const int m = u >> 8, c = ((u >> 2) & 63) + it * 64, w = u & 3;
+        xr[i] = c < KS ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + c * 32 + w * 8) : u32x4{0, 0, 0, 0};
+      }
     }
-  }
-  __syncthreads();
+  };
+  auto xstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int u = tid + i * T;
+      if (u < XUNITS) {
+        const int m = u >> 8, c = (u >> 2) & 63, w = u & 3;
+        xwin[buf][(m * 4 + w) * 64 + c] = xr[i];
+      }
+    }
+  };
+
+  // weight stage of iteration `it`: one chunk per row and its scale / zero bits
+  auto load = [&](int it, Stage<R, GPC>& st) {
+    const int c = min(it * 64 + lane, KS - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) st.w[r] = __builtin_nontemporal_load(prow[r] + c);
+    if constexpr (META == META_GROUP) {
+#pragma unroll
+      for (int q = 0; q < GPC; ++q) {
+        const int G = (c * 32 + q * 16) >> log2g;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          st.s[r][q] = srow[r][G];
+          st.z[r][q] = zrow[r][G];
+        }
+      }
+    }
+  };
 
   float acc[R][M];
 #pragma unroll
@@ -109,76 +151,75 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __rest
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  for (int it = 0; it < iters; ++it) {
-    const int c = it * 64 + lane;
-    const bool valid = c < KS;
-    const int cc = valid ? c : KS - 1;
-
-    int g0 = 0;
+  DqConst rc[R];
+  auto compute = [&](int it, const Stage<R, GPC>& st, int buf) {
+    if (it * 64 + lane >= KS) return;
+    DqConst dc[R][GPC];
     if constexpr (META == META_GROUP) {
-      g0 = (it * 2048) / g;
-      for (int e = lane; e < R * gpi; e += 64) {
-        const int r = e / gpi;
-        const int G = min(g0 + (e - r * gpi), gpr - 1);
-        const size_t mi = (size_t)rows[r] * gpr + G;
-        const DqConst d = dq_const(scales[mi], zeros[mi]);
-        DqEntry t;
-        t.s24 = d.s24;
-        t.s20 = d.s20;
-        t.nzs = d.nzs;
-        t.pad = 0.0f;
-        tbl[e] = t;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-
-    // prefetch the next iteration's chunks
-    u32x4 nv[R];
-    const bool more = it + 1 < iters;
-    if (more) {
-      const int cn = min(c + 64, KS - 1);
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        nv[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(packed + (size_t)rows[r] * (K >> 3)) + cn);
+#pragma unroll
+        for (int q = 0; q < GPC; ++q) dc[r][q] = dq_const_mix(st.s[r][q], st.z[r][q]);
     }
-
-    if (valid) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4 xv[M];
+    for (int w = 0; w < 4; ++w) {
+      u32x4 xv[M];
 #pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = xs[(m * 4 + w) * KS + cc];
+      for (int m = 0; m < M; ++m) xv[m] = xwin[buf][(m * 4 + w) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          DqConst d;
-          if constexpr (META == META_GROUP) {
-            const DqEntry t = tbl[r * gpi + ((cc * 32 + w * 8) / g - g0)];
-            d.s24 = t.s24;
-            d.s20 = t.s20;
-            d.nzs = t.nzs;
-          } else {
-            d = rc[r];
-          }
-          uint32_t bw[4];
-          dq_word_bf16(wv[r][w], d, bw);
+      for (int r = 0; r < R; ++r) {
+        uint32_t bw[4];
+        if constexpr (META == META_GROUP)
+          dq_word_bf16(st.w[r][w], dc[r][GPC == 2 ? w / 2 : 0], bw);
+        else
+          dq_word_bf16(st.w[r][w], rc[r], bw);
 #pragma unroll
-          for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[r][m] = dot2_bf16(bw[i], xv[m][i], acc[r][m]);
-        }
+          for (int i = 0; i < 4; ++i) acc[r][m] = dot2_bf16(bw[i], xv[m][i], acc[r][m]);
       }
     }
-    if (more) {
+  };
+
+  Stage<R, GPC> A, B;
+  xload(0);
+  load(0, A);
+  if constexpr (META != META_GROUP) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) wv[r] = nv[r];
+    for (int r = 0; r < R; ++r) {
+      const int mi = META == META_GLOBAL ? 0 : min(row0 + r, N - 1);
+      rc[r] = dq_const_mix(scales[mi], zeros[mi]);
     }
-    if constexpr (META == META_GROUP) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+  }
+  xstore(0);
+  __syncthreads();
+
+  // Two register stages, unrolled by two so the in-flight stage is never copied.  The
+  // next X window is requested before the next weight stage, so storing it to LDS never
+  // waits for the weights; the loop body issues exactly one weight stage while consuming
+  // the other (no conditional loads), and the tail is peeled.
+  int it = 0;
+  for (; it + 2 < iters; it += 2) {
+    xload(it + 1);
+    load(it + 1, B);
+    compute(it, A, 0);
+    xstore(1);
+    __syncthreads();
+    xload(it + 2);
+    load(it + 2, A);
+    compute(it + 1, B, 1);
+    xstore(0);
+    __syncthreads();
+  }
+  if (it + 1 < iters) {
+    xload(it + 1);
+    load(it + 1, B);
+    compute(it, A, 0);
+    xstore(1);
+    __syncthreads();
+    compute(it + 1, B, 1);
+  } else {
+    compute(it, A, 0);
   }
 
   // reduce R x MP partial sums across the wave (MP = M padded to a power of two)
@@ -212,52 +253,33 @@ struct GemvPlan {
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
 
 GemvPlan plan(const MmArgs& a) {
+  // rows per wave and waves per block: keep >= 256 blocks (one per CU) in flight
   GemvPlan p;
-  const size_t xbytes = (size_t)a.M * a.K * 2;
-  // rows per wave: keep at least ~512 waves in flight
-  p.R = a.N >= 512 * 4 ? 4 : (a.N >= 512 * 2 ? 2 : 1);
-  // waves per block: enough waves per CU despite the X copy each block holds
-  p.waves = xbytes <= 40 * 1024 ? 4 : (xbytes <= 72 * 1024 ? 8 : 16);
-  const int gpi = a.mode == W4_MODE_GROUPWISE ? (a.group >= 2048 ? 1 : 2048 / a.group) : 0;
-  p.lds = xbytes + (size_t)p.waves * p.R * gpi * sizeof(DqEntry);
+  p.waves = 8;
+  p.R = a.N >= 16 * 512 ? 2 : 1;
+  if (a.N < 8 * 256) p.waves = 4;
+  p.lds = (size_t)2 * a.M * 4 * 64 * 16;
   return p;
 }
 
 template <int M, int R, int META, int WAVES>
 hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  auto k = gemv_kernel<M, R, META, WAVES>;
-  if (p.lds > 64 * 1024) {
-    // opt in to the large LDS footprint (once per kernel instantiation)
-    static std::atomic<size_t> granted{0};
-    if (granted.load() < p.lds) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
-      if (e != hipSuccess) return e;
-      granted.store(p.lds);
-    }
-  }
+  auto k = (META == META_GROUP && a.group == 16) ? gemv_kernel<M, R, META, WAVES, 2> : gemv_kernel<M, R, META, WAVES, 1>;
   const int rows_per_block = R * WAVES;
   const dim3 grid((unsigned)((a.N + rows_per_block - 1) / rows_per_block));
-  k<<<grid, WAVES * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.N, (int)a.K, a.group);
+  const int log2g = 31 - __builtin_clz((unsigned)a.group);  // GROUPWISE g is a power of two
+  k<<<grid, WAVES * 64, 0, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.N, (int)a.K, log2g);
   return hipGetLastError();
 }
 
 template <int M, int R, int META>
 hipError_t run_w(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  switch (p.waves) {
-    case 4: return run<M, R, META, 4>(a, p, st);
-    case 8: return run<M, R, META, 8>(a, p, st);
-    default: return run<M, R, META, 16>(a, p, st);
-  }
+  return p.waves == 4 ? run<M, R, META, 4>(a, p, st) : run<M, R, META, 8>(a, p, st);
 }
 
 template <int M, int META>
 hipError_t run_r(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  switch (p.R) {
-    case 4: return run_w<M, 4, META>(a, p, st);
-    case 2: return run_w<M, 2, META>(a, p, st);
-    default: return run_w<M, 1, META>(a, p, st);
-  }
+  return p.R == 2 ? run_w<M, 2, META>(a, p, st) : run_w<M, 1, META>(a, p, st);
 }
 
 template <int M>
