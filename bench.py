@@ -291,6 +291,8 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip the GEMM and quantize blocks")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--details", default=None, help="write per-point results (JSON) to this path")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device-to-device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -308,6 +310,14 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy calibration: 268435456 bytes read and written once")
 
     g = bench_gemv(torch, w4, synth, args)
     log(f"GEMV sweep: {g['value']:.1f} GB/s per step, {g['achieved_gbs']:.1f} GB/s kernel-only")

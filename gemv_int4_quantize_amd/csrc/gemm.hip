@@ -7,109 +7,123 @@
 // the transposed product reads the same packed weights, scales and zeros);
 // "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560).
 //
-// Structure (one workgroup = WM x WN waves, output tile BM x BN, contraction step 32):
+// Structure (one workgroup = WM x WN waves, output tile BM x BN, contraction step BK):
 //   * the activation tile (X or dY, contraction along its rows) goes global -> LDS;
 //   * the packed weight tile is loaded to registers, dequantized in registers with
 //     v_fma_mix_f32 + v_cvt_pk_bf16_f32, and written to LDS as a bf16 tile whose
-//     rows are output columns and whose 32 columns are the contraction, so each MFMA
+//     rows are output columns and whose BK columns are the contraction, so each MFMA
 //     operand is one 16-byte LDS read in both directions.  Non-transposed, a packed
 //     word already runs along the contraction; transposed, each thread dequantizes a
-//     column of RPT rows of one word and writes it across the contraction axis;
-//   * two LDS stages: the global loads of step k+1 are in flight during the MFMAs of
-//     step k, and their dequantization follows them; one barrier per step;
-//   * LDS rows are 80 bytes (64 + 16 pad) so the 16 rows read by one MFMA operand load
-//     fall in distinct banks;
-//   * v_mfma_f32_16x16x32_bf16: lane l holds row (l % 16), contraction slots
-//     8 (l / 16) .. +7 of A, column (l % 16) and the same slots of B, and rows
-//     4 (l / 16) .. +3 of column (l % 16) of the result.
+//     column of rows of one word and writes it across the contraction axis;
+//   * three LDS stages: the global loads of step k+2 are in flight during the MFMAs of
+//     steps k and k+1, and are dequantized into LDS at the end of step k+1; one
+//     barrier per step;
+//   * LDS rows are padded by 16 bytes so the rows read by one MFMA operand load fall
+//     in distinct banks;
+//   * v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains twice the rate of the
+//     16x16x32 form): lane l holds row (l % 32), contraction slots 8 (l / 32) .. +7
+//     of A, column (l % 32) and the same slots of B; result register r of a 32x32
+//     block is row 8 (r / 4) + 4 (l / 32) + (r % 4) of column l % 32.
 #include "common.h"
 #include "launch.h"
 
+#include <cstdlib>
+
 namespace w4 {
 
-constexpr int kBK = 32;       // contraction per stage
-constexpr int kLdsRow = 40;   // bf16 per LDS row (32 + 8 pad)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <bool TRANS, int WM, int WN, int FM, int FN, int META>
+// LDS rows hold BK contraction values plus 8 bf16 of padding: a row stride of
+// (BK + 8) * 2 bytes puts the 16-byte operand reads of consecutive rows in distinct banks.
+template <int BK>
+constexpr int lds_row() { return BK + 8; }
+
+// MPT: scale / zero pairs a thread loads per stage in the non-transposed mode: 1 when
+// one group covers all of its words (rowwise, global, or g >= its span), else one per word.
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A,
                                                             const int32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const uint16_t* __restrict__ zeros,
                                                             const float* __restrict__ bias, float* __restrict__ Y,
-                                                            int M, int N, int K, int g) {
+                                                            int M, int N, int K, int log2g) {
   constexpr int T = WM * WN * 64;
-  constexpr int BM = WM * FM * 16;
-  constexpr int BN = WN * FN * 16;
-  constexpr int A_UNITS = BM * 4 / T;  // 16-byte units of the activation tile per thread
-  static_assert(A_UNITS >= 1 && BM * 4 % T == 0, "activation tile split");
-  constexpr int W_PER_T = BN * 4 / T;  // packed words per thread per stage
-  static_assert(W_PER_T >= 1 && W_PER_T <= 4 && BN * 4 % T == 0, "weight tile split");
+  constexpr int BM = WM * FM * 32;
+  constexpr int BN = WN * FN * 32;
+  constexpr int LR = lds_row<BK>();
+  constexpr int SLOTS = BK / 8;                 // 16-byte units per activation row per stage
+  constexpr int A_UNITS = BM * SLOTS / T;       // activation units per thread per stage
+  static_assert(A_UNITS >= 1 && BM * SLOTS % T == 0, "activation tile split");
+  constexpr int W_PER_T = BN * SLOTS / T;       // packed words per thread per stage
+  static_assert(W_PER_T >= 1 && W_PER_T <= 8 && BN * SLOTS % T == 0, "weight tile split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLdsRow];
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* As = smem;                          // [3][BM][LR]
+  uint16_t* Bs = smem + 3 * BM * LR;            // [3][BN][LR]
 
   const int L = TRANS ? N : K;      // contraction length
   const int OUTC = TRANS ? K : N;   // output columns
   const int KW = K >> 3;            // packed words per weight row
-  const int gpr = META == META_GROUP ? K / g : 1;
+  const int gpr = META == META_GROUP ? K >> log2g : 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM;
   const int c0 = blockIdx.x * BN;
-  const int KT = (L + kBK - 1) / kBK;
+  const int KT = (L + BK - 1) / BK;
 
-  // ---- staging registers
-  u32x4 areg[A_UNITS];
-  uint32_t wreg[W_PER_T];
-  uint16_t sreg[W_PER_T], zreg[W_PER_T];
+  // ---- staging registers: one stage of raw global data (two buffers alternate)
+  struct Regs {
+    u32x4 a[A_UNITS];
+    uint32_t w[W_PER_T];
+    uint16_t s[W_PER_T], z[W_PER_T];
+  };
 
   auto meta_index = [&](int n, int wcol) -> size_t {
     if constexpr (META == META_GLOBAL) return 0;
     else if constexpr (META == META_ROW) return (size_t)n;
-    else return (size_t)n * gpr + (wcol * 8) / g;
+    else return (size_t)n * gpr + ((wcol * 8) >> log2g);
   };
 
-  auto load_stage = [&](int kt) {
-    const int l0 = kt * kBK;
+  auto load_stage = [&](int kt, Regs& R) {
+    const int l0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;
-      const int row = u >> 2, slot = u & 3;
+      const int row = u / SLOTS, slot = u % SLOTS;
       const int m = min(m0 + row, M - 1);
-      const int l = l0 + slot * 8;
-      if (l < L) {
-        areg[i] = *reinterpret_cast<const u32x4*>(A + (size_t)m * L + l);
-      } else {
-        areg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int l = min(l0 + slot * 8, L - 8);  // past the end of the contraction: zeroed at store
+      R.a[i] = *reinterpret_cast<const u32x4*>(A + (size_t)m * L + l);
     }
     if constexpr (!TRANS) {
-      // rows = output columns n, words along the contraction
-      constexpr int TPR = 4 / W_PER_T;  // threads per row
+      // rows = output columns n; each thread takes W_PER_T consecutive words of one row
+      constexpr int TPR = SLOTS / W_PER_T;  // threads per row
       const int row = tid / TPR;
       const int w0 = (tid % TPR) * W_PER_T;
       const int n = min(c0 + row, N - 1);
       const int wc = (l0 >> 3) + w0;
       const int32_t* src = packed + (size_t)n * KW + wc;
-      if constexpr (W_PER_T == 4) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-        wreg[0] = v[0]; wreg[1] = v[1]; wreg[2] = v[2]; wreg[3] = v[3];
+      if constexpr (W_PER_T >= 4) {
+#pragma unroll
+        for (int h = 0; h < W_PER_T / 4; ++h) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + h);
+          R.w[4 * h] = v[0]; R.w[4 * h + 1] = v[1]; R.w[4 * h + 2] = v[2]; R.w[4 * h + 3] = v[3];
+        }
       } else if constexpr (W_PER_T == 2) {
         const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
-        wreg[0] = v[0]; wreg[1] = v[1];
+        R.w[0] = v[0]; R.w[1] = v[1];
       } else {
-        wreg[0] = (uint32_t)__builtin_nontemporal_load(src);
+        R.w[0] = (uint32_t)__builtin_nontemporal_load(src);
       }
 #pragma unroll
-      for (int i = 0; i < W_PER_T; ++i) {
+      for (int i = 0; i < MPT; ++i) {
         const size_t mi = meta_index(n, wc + i);
-        sreg[i] = scales[mi];
-        zreg[i] = zeros[mi];
+        R.s[i] = scales[mi];
+        R.z[i] = zeros[mi];
       }
     } else {
-      // rows = contraction n, words = output columns k (8 per word)
+      // rows = contraction n (W_PER_T consecutive rows per thread), one word = 8 output columns
       constexpr int WCOLS = BN / 8;
       const int wc = tid % WCOLS;
       const int rb = tid / WCOLS;
@@ -117,45 +131,52 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < W_PER_T; ++i) {
         const int n = min(l0 + rb * W_PER_T + i, N - 1);
-        wreg[i] = (uint32_t)__builtin_nontemporal_load(packed + (size_t)n * KW + wcol);
+        R.w[i] = (uint32_t)__builtin_nontemporal_load(packed + (size_t)n * KW + wcol);
         const size_t mi = meta_index(n, wcol);
-        sreg[i] = scales[mi];
-        zreg[i] = zeros[mi];
+        R.s[i] = scales[mi];
+        R.z[i] = zeros[mi];
       }
     }
   };
 
-  auto store_stage = [&](int buf) {
-    uint16_t* as = As[buf];
-    uint16_t* bs = Bs[buf];
+  auto store_stage = [&](int kt, const Regs& R, int buf) {
+    uint16_t* as = As + buf * BM * LR;
+    uint16_t* bs = Bs + buf * BN * LR;
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;
-      const int row = u >> 2, slot = u & 3;
-      *reinterpret_cast<u32x4*>(as + row * kLdsRow + slot * 8) = areg[i];
+      const int row = u / SLOTS, slot = u % SLOTS;
+      const bool in = TRANS ? kt * BK + slot * 8 < L : true;
+      *reinterpret_cast<u32x4*>(as + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (!TRANS) {
-      constexpr int TPR = 4 / W_PER_T;
+      constexpr int TPR = SLOTS / W_PER_T;
       const int row = tid / TPR;
       const int w0 = (tid % TPR) * W_PER_T;
+      DqConst d0;
+      if constexpr (MPT == 1) d0 = dq_const(R.s[0], R.z[0]);
 #pragma unroll
       for (int i = 0; i < W_PER_T; ++i) {
-        const DqConst d = dq_const(sreg[i], zreg[i]);
         uint32_t o[4];
-        dq_word_bf16(wreg[i], d, o);
-        *reinterpret_cast<u32x4*>(bs + row * kLdsRow + (w0 + i) * 8) = u32x4{o[0], o[1], o[2], o[3]};
+        dq_word_bf16(R.w[i], MPT == 1 ? d0 : dq_const(R.s[i], R.z[i]), o);
+        *reinterpret_cast<u32x4*>(bs + row * LR + (w0 + i) * 8) = u32x4{o[0], o[1], o[2], o[3]};
       }
     } else {
+      // dequantize a column of W_PER_T rows x 8 output columns and write it across the
+      // contraction axis: output column k = 8 wc + j gets W_PER_T consecutive n values
       constexpr int WCOLS = BN / 8;
       const int wc = tid % WCOLS;
       const int rb = tid / WCOLS;
       float v[W_PER_T][8];
 #pragma unroll
-      for (int i = 0; i < W_PER_T; ++i) dq_word_f32(wreg[i], dq_const(sreg[i], zreg[i]), v[i]);
+      for (int i = 0; i < W_PER_T; ++i) dq_word_f32(R.w[i], dq_const(R.s[i], R.z[i]), v[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint16_t* dst = bs + (wc * 8 + j) * kLdsRow + rb * W_PER_T;
-        if constexpr (W_PER_T == 4) {
+        uint16_t* dst = bs + (wc * 8 + j) * LR + rb * W_PER_T;
+        if constexpr (W_PER_T == 8) {
+          *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
+                                                 pack_bf16x2(v[4][j], v[5][j]), pack_bf16x2(v[6][j], v[7][j])};
+        } else if constexpr (W_PER_T == 4) {
           *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j])};
         } else if constexpr (W_PER_T == 2) {
           *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0][j], v[1][j]);
@@ -166,50 +187,90 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     }
   };
 
-  f32x4 acc[FM][FN];
+  f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_stage(0);
-  store_stage(0);
+  // v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A and column (l % 32) of B,
+  // contraction slots 8 (l / 32) .. +7 of the 16-wide step
+  const int lr = lane & 31;
+  const int lk = (lane >> 5) * 8;
+  auto compute = [&](int buf) {
+    const uint16_t* as = As + buf * BM * LR + (wm * FM * 32 + lr) * LR + lk;
+    const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR + lk;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LR + kk * 16);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + kk * 16);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Three LDS stages and two register stages: the global loads of step k + 2 are issued
+  // before the MFMAs of step k and stored (dequantized) to LDS at the end of step k + 1,
+  // so each load has two steps of MFMA work to arrive.  Unrolled by two so the register
+  // stage in flight is never copied; every load in the loop body is unconditional (the
+  // compiler's wait counts then keep the other stage in flight) and the tail is peeled.
+  Regs R0, R1;
+  load_stage(0, R0);
+  load_stage(min(1, KT - 1), R1);
+  store_stage(0, R0, 0);
   __syncthreads();
-
-  const int lr = lane & 15;        // operand row (A) / column (B)
-  const int lk = (lane >> 4) * 8;  // contraction slot
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) load_stage(kt + 1);
-    const uint16_t* as = As[buf] + (wm * FM * 16 + lr) * kLdsRow + lk;
-    const uint16_t* bs = Bs[buf] + (wn * FN * 16 + lr) * kLdsRow + lk;
-    bf16x8 af[FM], bfr[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 16 * kLdsRow);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 16 * kLdsRow);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    if (more) store_stage(buf ^ 1);
+  int kt = 0;
+  for (; kt + 4 <= KT; kt += 2) {
+    load_stage(kt + 2, R0);
+    compute(kt % 3);
+    store_stage(kt + 1, R1, (kt + 1) % 3);
+    __syncthreads();
+    load_stage(kt + 3, R1);
+    compute((kt + 1) % 3);
+    store_stage(kt + 2, R0, (kt + 2) % 3);
     __syncthreads();
   }
+  const int rem = KT - kt;  // 1, 2 or 3 steps left; R1 holds step kt + 1
+  if (rem == 3) {
+    load_stage(kt + 2, R0);
+    compute(kt % 3);
+    store_stage(kt + 1, R1, (kt + 1) % 3);
+    __syncthreads();
+    compute((kt + 1) % 3);
+    store_stage(kt + 2, R0, (kt + 2) % 3);
+    __syncthreads();
+    compute((kt + 2) % 3);
+  } else if (rem == 2) {
+    compute(kt % 3);
+    store_stage(kt + 1, R1, (kt + 1) % 3);
+    __syncthreads();
+    compute((kt + 1) % 3);
+  } else {
+    compute(kt % 3);
+  }
 
-  // ---- epilogue: bias in fp32, masked fp32 stores
-  const int rbase = m0 + wm * FM * 16 + (lane >> 4) * 4;
-  const int cbase = c0 + wn * FN * 16 + lr;
+  // ---- epilogue: bias in fp32, masked fp32 stores.  Result register r of a 32x32
+  // block sits at row 8 (r / 4) + 4 (lane / 32) + (r % 4), column lane % 32.
+  const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
+  const int cbase = c0 + wn * FN * 32 + lr;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int c = cbase + j * 16;
+    const int c = cbase + j * 32;
     if (c >= OUTC) continue;
     const float b = bias != nullptr ? bias[c] : 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = rbase + i * 16 + r;
+      for (int r = 0; r < 16; ++r) {
+        const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
         if (m < M) Y[(size_t)m * OUTC + c] = acc[i][j][r] + b;
       }
     }
@@ -221,55 +282,85 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 namespace {
 
 struct Cfg {
-  int wm, wn, fm, fn;
+  int wm, wn, fm, fn, bk;
   const char* name_nt;
   const char* name_t;
 };
 
+// wave tile (fm x 32) x (fn x 32), block tile (wm * fm * 32) x (wn * fn * 32)
 constexpr Cfg kCfgs[] = {
-    {2, 2, 8, 4, "gemm_nt_256x128", "gemm_t_256x128"},
-    {1, 4, 8, 4, "gemm_nt_128x256", "gemm_t_128x256"},
-    {2, 2, 4, 4, "gemm_nt_128x128", "gemm_t_128x128"},
+    {2, 2, 4, 4, 32, "gemm_nt_256x256", "gemm_t_256x256"},
+    {2, 2, 4, 2, 32, "gemm_nt_256x128", "gemm_t_256x128"},
+    {2, 2, 2, 2, 32, "gemm_nt_128x128", "gemm_t_128x128"},
+    {4, 2, 2, 2, 32, "gemm_nt_256x128w8", "gemm_t_256x128w8"},
+    {2, 4, 2, 2, 32, "gemm_nt_128x256w8", "gemm_t_128x256w8"},
 };
+constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 int pick(const MmArgs& a) {
+  // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
+  static const int forced = [] {
+    const char* e = getenv("W4A16_GEMM_CFG");
+    return e != nullptr ? atoi(e) : -1;
+  }();
+  if (forced >= 0 && forced < kNumCfgs) return forced;
   const int64_t outc = a.transposed ? a.K : a.N;
   auto tiles = [&](const Cfg& c) {
-    const int64_t bm = c.wm * c.fm * 16, bn = c.wn * c.fn * 16;
+    const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
     return ((a.M + bm - 1) / bm) * ((outc + bn - 1) / bn);
   };
-  if (a.M > 128 && tiles(kCfgs[0]) >= 256) return 0;
-  if (tiles(kCfgs[1]) >= 256) return 1;
+  // measured on MI355X at the fine-tune shapes: 8 waves of 128x64 for the forward
+  // product, 4 waves of 128x64 for the transposed one (its dequantize-and-transpose
+  // staging favours the larger per-thread share)
+  const int big = a.transposed ? 1 : 3;
+  if (a.M > 128 && tiles(kCfgs[big]) >= 256) return big;
   return 2;
 }
 
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
 
-template <bool TRANS, int WM, int WN, int FM, int FN, int META>
+size_t lds_bytes(const Cfg& c) {
+  return (size_t)3 * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
+}
+
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META>
 hipError_t run(const MmArgs& a, hipStream_t st) {
-  constexpr int BM = WM * FM * 16, BN = WN * FN * 16;
+  constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
+  constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
+  // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
+  const bool one = TRANS || META != META_GROUP || a.group >= 8 * WPT;
+  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1> : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT>;
+  const size_t lds = (size_t)3 * (BM + BN) * (BK + 8) * 2;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
   const int64_t outc = TRANS ? a.K : a.N;
   const dim3 grid((unsigned)((outc + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
-  gemm_kernel<TRANS, WM, WN, FM, FN, META><<<grid, WM * WN * 64, 0, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias,
-                                                                          a.Y, (int)a.M, (int)a.N, (int)a.K, a.group);
+  const int log2g = 31 - __builtin_clz((unsigned)a.group);
+  k<<<grid, WM * WN * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.M, (int)a.N, (int)a.K,
+                                      log2g);
   return hipGetLastError();
 }
 
-template <bool TRANS, int WM, int WN, int FM, int FN>
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK>
 hipError_t run_meta(const MmArgs& a, hipStream_t st) {
   switch (meta_kind(a.mode)) {
-    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, META_GLOBAL>(a, st);
-    case META_ROW: return run<TRANS, WM, WN, FM, FN, META_ROW>(a, st);
-    default: return run<TRANS, WM, WN, FM, FN, META_GROUP>(a, st);
+    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, META_GLOBAL>(a, st);
+    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, META_ROW>(a, st);
+    default: return run<TRANS, WM, WN, FM, FN, BK, META_GROUP>(a, st);
   }
 }
 
 template <bool TRANS>
 hipError_t run_cfg(const MmArgs& a, hipStream_t st) {
   switch (pick(a)) {
-    case 0: return run_meta<TRANS, 2, 2, 8, 4>(a, st);
-    case 1: return run_meta<TRANS, 1, 4, 8, 4>(a, st);
-    default: return run_meta<TRANS, 2, 2, 4, 4>(a, st);
+    case 0: return run_meta<TRANS, 2, 2, 4, 4, 32>(a, st);
+    case 1: return run_meta<TRANS, 2, 2, 4, 2, 32>(a, st);
+    case 3: return run_meta<TRANS, 4, 2, 2, 2, 32>(a, st);
+    case 4: return run_meta<TRANS, 2, 4, 2, 2, 32>(a, st);
+    default: return run_meta<TRANS, 2, 2, 2, 2, 32>(a, st);
   }
 }
 
@@ -280,10 +371,7 @@ const char* gemm_name(const MmArgs& a) {
   return a.transposed ? c.name_t : c.name_nt;
 }
 
-size_t gemm_lds_bytes(const MmArgs& a) {
-  const Cfg& c = kCfgs[pick(a)];
-  return (size_t)2 * (c.wm * c.fm * 16 + c.wn * c.fn * 16) * kLdsRow * 2;
-}
+size_t gemm_lds_bytes(const MmArgs& a) { return lds_bytes(kCfgs[pick(a)]); }
 
 hipError_t launch_gemm(const MmArgs& a, hipStream_t st) {
   return a.transposed ? run_cfg<true>(a, st) : run_cfg<false>(a, st);
