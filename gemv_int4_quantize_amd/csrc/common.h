@@ -72,6 +72,19 @@ __device__ __forceinline__ DqConst dq_const(uint32_t s_bits, uint32_t z_bits) {
   return c;
 }
 
+// Dequantization constants from raw fp16 bits, three v_fma_mix_f32 (exact):
+// s * 2^24, s * 2^20 and -(z * s).
+__device__ __forceinline__ DqConst dq_const_mix(uint16_t s_bits, uint16_t z_bits) {
+  DqConst c;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s24) : "v"(s_bits), "v"(16777216.0f));
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s20) : "v"(s_bits), "v"(1048576.0f));
+  asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(c.nzs) : "v"(z_bits), "v"(s_bits));
+  return c;
+}
+
+// One iteration covers 2048 columns: 64 lanes x one 16-byte chunk (32 codes) per row.
+constexpr int kIterCols = 2048;
+
 // One packed word (8 codes along K) -> 4 dwords of bf16 pairs in K order:
 // out[i] = (w[2i], w[2i+1]).  17 VALU instructions.
 __device__ __forceinline__ void dq_word_bf16(uint32_t w, const DqConst& c, uint32_t out[4]) {

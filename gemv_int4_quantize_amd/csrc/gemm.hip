@@ -40,7 +40,8 @@ constexpr int lds_row() { return BK + 8; }
 
 // MPT: scale / zero pairs a thread loads per stage in the non-transposed mode: 1 when
 // one group covers all of its words (rowwise, global, or g >= its span), else one per word.
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT>
+// STAGES: 2 (loads of step k+1 in flight during step k) or 3 (loads of step k+2).
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A,
                                                             const int32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
@@ -58,8 +59,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   static_assert(W_PER_T >= 1 && W_PER_T <= 8 && BN * SLOTS % T == 0, "weight tile split");
 
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* As = smem;                          // [3][BM][LR]
-  uint16_t* Bs = smem + 3 * BM * LR;            // [3][BN][LR]
+  uint16_t* As = smem;                          // [STAGES][BM][LR]
+  uint16_t* Bs = smem + STAGES * BM * LR;       // [STAGES][BN][LR]
 
   const int L = TRANS ? N : K;      // contraction length
   const int OUTC = TRANS ? K : N;   // output columns
@@ -154,11 +155,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       const int row = tid / TPR;
       const int w0 = (tid % TPR) * W_PER_T;
       DqConst d0;
-      if constexpr (MPT == 1) d0 = dq_const(R.s[0], R.z[0]);
+      if constexpr (MPT == 1) d0 = dq_const_mix(R.s[0], R.z[0]);
 #pragma unroll
       for (int i = 0; i < W_PER_T; ++i) {
         uint32_t o[4];
-        dq_word_bf16(R.w[i], MPT == 1 ? d0 : dq_const(R.s[i], R.z[i]), o);
+        dq_word_bf16(R.w[i], MPT == 1 ? d0 : dq_const_mix(R.s[i], R.z[i]), o);
         *reinterpret_cast<u32x4*>(bs + row * LR + (w0 + i) * 8) = u32x4{o[0], o[1], o[2], o[3]};
       }
     } else {
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       const int rb = tid / WCOLS;
       float v[W_PER_T][8];
 #pragma unroll
-      for (int i = 0; i < W_PER_T; ++i) dq_word_f32(R.w[i], dq_const(R.s[i], R.z[i]), v[i]);
+      for (int i = 0; i < W_PER_T; ++i) dq_word_f32(R.w[i], dq_const_mix(R.s[i], R.z[i]), v[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint16_t* dst = bs + (wc * 8 + j) * LR + rb * W_PER_T;
@@ -217,44 +218,60 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     }
   };
 
-  // Three LDS stages and two register stages: the global loads of step k + 2 are issued
-  // before the MFMAs of step k and stored (dequantized) to LDS at the end of step k + 1,
-  // so each load has two steps of MFMA work to arrive.  Unrolled by two so the register
-  // stage in flight is never copied; every load in the loop body is unconditional (the
-  // compiler's wait counts then keep the other stage in flight) and the tail is peeled.
-  Regs R0, R1;
-  load_stage(0, R0);
-  load_stage(min(1, KT - 1), R1);
-  store_stage(0, R0, 0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 4 <= KT; kt += 2) {
-    load_stage(kt + 2, R0);
-    compute(kt % 3);
-    store_stage(kt + 1, R1, (kt + 1) % 3);
+  if constexpr (STAGES == 2) {
+    // Two LDS stages, one register stage: the loads of step k+1 are issued before the
+    // MFMAs of step k and dequantized into the other LDS buffer after them.
+    Regs R0;
+    load_stage(0, R0);
+    store_stage(0, R0, 0);
     __syncthreads();
-    load_stage(kt + 3, R1);
-    compute((kt + 1) % 3);
-    store_stage(kt + 2, R0, (kt + 2) % 3);
-    __syncthreads();
-  }
-  const int rem = KT - kt;  // 1, 2 or 3 steps left; R1 holds step kt + 1
-  if (rem == 3) {
-    load_stage(kt + 2, R0);
-    compute(kt % 3);
-    store_stage(kt + 1, R1, (kt + 1) % 3);
-    __syncthreads();
-    compute((kt + 1) % 3);
-    store_stage(kt + 2, R0, (kt + 2) % 3);
-    __syncthreads();
-    compute((kt + 2) % 3);
-  } else if (rem == 2) {
-    compute(kt % 3);
-    store_stage(kt + 1, R1, (kt + 1) % 3);
-    __syncthreads();
-    compute((kt + 1) % 3);
+    for (int kt = 0; kt < KT; ++kt) {
+      const bool more = kt + 1 < KT;
+      if (more) load_stage(kt + 1, R0);
+      compute(kt & 1);
+      if (more) store_stage(kt + 1, R0, (kt + 1) & 1);
+      __syncthreads();
+    }
   } else {
-    compute(kt % 3);
+    // Three LDS stages and two register stages: the global loads of step k + 2 are issued
+    // before the MFMAs of step k and stored (dequantized) to LDS at the end of step k + 1,
+    // so each load has two steps of MFMA work to arrive.  Unrolled by two so the register
+    // stage in flight is never copied; every load in the loop body is unconditional (the
+    // compiler's wait counts then keep the other stage in flight) and the tail is peeled.
+    Regs R0, R1;
+    load_stage(0, R0);
+    load_stage(min(1, KT - 1), R1);
+    store_stage(0, R0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 4 <= KT; kt += 2) {
+      load_stage(kt + 2, R0);
+      compute(kt % 3);
+      store_stage(kt + 1, R1, (kt + 1) % 3);
+      __syncthreads();
+      load_stage(kt + 3, R1);
+      compute((kt + 1) % 3);
+      store_stage(kt + 2, R0, (kt + 2) % 3);
+      __syncthreads();
+    }
+    const int rem = KT - kt;  // 1, 2 or 3 steps left; R1 holds step kt + 1
+    if (rem == 3) {
+      load_stage(kt + 2, R0);
+      compute(kt % 3);
+      store_stage(kt + 1, R1, (kt + 1) % 3);
+      __syncthreads();
+      compute((kt + 1) % 3);
+      store_stage(kt + 2, R0, (kt + 2) % 3);
+      __syncthreads();
+      compute((kt + 2) % 3);
+    } else if (rem == 2) {
+      compute(kt % 3);
+      store_stage(kt + 1, R1, (kt + 1) % 3);
+      __syncthreads();
+      compute((kt + 1) % 3);
+    } else {
+      compute(kt % 3);
+    }
   }
 
   // ---- epilogue: bias in fp32, masked fp32 stores.  Result register r of a 32x32
@@ -282,19 +299,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 namespace {
 
 struct Cfg {
-  int wm, wn, fm, fn, bk;
+  int wm, wn, fm, fn, bk, stages;
   const char* name_nt;
   const char* name_t;
 };
 
 // wave tile (fm x 32) x (fn x 32), block tile (wm * fm * 32) x (wn * fn * 32)
-constexpr Cfg kCfgs[] = {
-    {2, 2, 4, 4, 32, "gemm_nt_256x256", "gemm_t_256x256"},
-    {2, 2, 4, 2, 32, "gemm_nt_256x128", "gemm_t_256x128"},
-    {2, 2, 2, 2, 32, "gemm_nt_128x128", "gemm_t_128x128"},
-    {4, 2, 2, 2, 32, "gemm_nt_256x128w8", "gemm_t_256x128w8"},
-    {2, 4, 2, 2, 32, "gemm_nt_128x256w8", "gemm_t_128x256w8"},
+// Tile configurations.  `eff_nt` / `eff_t`: throughput of a full tile relative to the
+// best one, measured on MI355X at the fine-tune shapes (M = 4096, groupwise g = 64).
+struct CfgEff {
+  float nt, t;
 };
+constexpr Cfg kCfgs[] = {
+    {2, 2, 4, 4, 64, 2, "gemm_nt_256x256", "gemm_t_256x256"},
+    {4, 2, 2, 2, 64, 2, "gemm_nt_256x128", "gemm_t_256x128"},
+    {2, 2, 2, 2, 32, 3, "gemm_nt_128x128", "gemm_t_128x128"},
+};
+constexpr CfgEff kEff[] = {{1.0f, 1.0f}, {0.87f, 0.82f}, {0.64f, 0.64f}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 int pick(const MmArgs& a) {
@@ -304,33 +325,42 @@ int pick(const MmArgs& a) {
     return e != nullptr ? atoi(e) : -1;
   }();
   if (forced >= 0 && forced < kNumCfgs) return forced;
+  // score = full-tile efficiency x how well the tiles fill the 256 CUs in whole waves
+  // x how much of the edge tiles is real work
   const int64_t outc = a.transposed ? a.K : a.N;
-  auto tiles = [&](const Cfg& c) {
+  int best = kNumCfgs - 1;
+  float best_score = -1.0f;
+  for (int i = 0; i < kNumCfgs; ++i) {
+    const Cfg& c = kCfgs[i];
     const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
-    return ((a.M + bm - 1) / bm) * ((outc + bn - 1) / bn);
-  };
-  // measured on MI355X at the fine-tune shapes: 8 waves of 128x64 for the forward
-  // product, 4 waves of 128x64 for the transposed one (its dequantize-and-transpose
-  // staging favours the larger per-thread share)
-  const int big = a.transposed ? 1 : 3;
-  if (a.M > 128 && tiles(kCfgs[big]) >= 256) return big;
-  return 2;
+    const int64_t tm = (a.M + bm - 1) / bm, tn = (outc + bn - 1) / bn;
+    const int64_t tiles = tm * tn;
+    const float waves = (float)((tiles + 255) / 256);
+    const float fill = (float)tiles / (256.0f * waves) * (float)a.M / (float)(tm * bm) * (float)outc / (float)(tn * bn);
+    const float score = fill * (a.transposed ? kEff[i].t : kEff[i].nt);
+    if (score > best_score) {
+      best_score = score;
+      best = i;
+    }
+  }
+  return best;
 }
 
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
 
 size_t lds_bytes(const Cfg& c) {
-  return (size_t)3 * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
+  return (size_t)c.stages * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
 }
 
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META>
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
 hipError_t run(const MmArgs& a, hipStream_t st) {
   constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
   // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
   const bool one = TRANS || META != META_GROUP || a.group >= 8 * WPT;
-  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1> : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT>;
-  const size_t lds = (size_t)3 * (BM + BN) * (BK + 8) * 2;
+  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES>
+               : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES>;
+  const size_t lds = (size_t)STAGES * (BM + BN) * (BK + 8) * 2;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -344,23 +374,21 @@ hipError_t run(const MmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK>
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>
 hipError_t run_meta(const MmArgs& a, hipStream_t st) {
   switch (meta_kind(a.mode)) {
-    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, META_GLOBAL>(a, st);
-    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, META_ROW>(a, st);
-    default: return run<TRANS, WM, WN, FM, FN, BK, META_GROUP>(a, st);
+    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GLOBAL>(a, st);
+    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_ROW>(a, st);
+    default: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GROUP>(a, st);
   }
 }
 
 template <bool TRANS>
 hipError_t run_cfg(const MmArgs& a, hipStream_t st) {
   switch (pick(a)) {
-    case 0: return run_meta<TRANS, 2, 2, 4, 4, 32>(a, st);
-    case 1: return run_meta<TRANS, 2, 2, 4, 2, 32>(a, st);
-    case 3: return run_meta<TRANS, 4, 2, 2, 2, 32>(a, st);
-    case 4: return run_meta<TRANS, 2, 4, 2, 2, 32>(a, st);
-    default: return run_meta<TRANS, 2, 2, 2, 2, 32>(a, st);
+    case 0: return run_meta<TRANS, 2, 2, 4, 4, 64, 2>(a, st);
+    case 1: return run_meta<TRANS, 4, 2, 2, 2, 64, 2>(a, st);
+    default: return run_meta<TRANS, 2, 2, 2, 2, 32, 3>(a, st);
   }
 }
 

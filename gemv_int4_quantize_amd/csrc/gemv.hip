@@ -57,19 +57,6 @@ struct Stage {
   uint16_t s[R][GPC], z[R][GPC];  // kept 16-bit: v_fma_mix_f32 reads the low half as fp16
 };
 
-// Dequantization constants from raw fp16 bits, three v_fma_mix_f32 (exact):
-// s * 2^24, s * 2^20 and -(z * s).
-__device__ __forceinline__ DqConst dq_const_mix(uint16_t s_bits, uint16_t z_bits) {
-  DqConst c;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s24) : "v"(s_bits), "v"(16777216.0f));
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s20) : "v"(s_bits), "v"(1048576.0f));
-  asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(c.nzs) : "v"(z_bits), "v"(s_bits));
-  return c;
-}
-
-// One iteration covers 2048 columns: 64 lanes x one 16-byte chunk (32 codes) per row.
-constexpr int kIterCols = 2048;
-
 template <int M, int R, int META, int WAVES, int GPC>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __restrict__ X,
                                                           const int32_t* __restrict__ packed,
