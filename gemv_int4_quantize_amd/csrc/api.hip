@@ -133,12 +133,19 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
   int s = check_desc(desc);
   if (s != W4_OK) return s;
   if (!bytes) return fail(W4_ERR_INVALID, "bytes is NULL");
-  (void)M;
   switch (op) {
     case W4_OP_QUANTIZE: *bytes = w4::quantize_workspace_bytes(desc->mode); break;
-    case W4_OP_MM:
-    case W4_OP_MM_T:
     case W4_OP_DEQUANTIZE: *bytes = 0; break;
+    case W4_OP_MM:
+    case W4_OP_MM_T: {
+      *bytes = 0;
+      if (M < 1 || M > ((int64_t)1 << 31) - 1 || desc->K % 32 != 0) break;
+      static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
+      const w4::MmArgs a = make_args(dummy, M, reinterpret_cast<const int32_t*>(dummy), dummy, dummy, desc,
+                                     op == W4_OP_MM_T, nullptr, nullptr);
+      if (!w4::gemv_supported(a, device_lds_limit())) *bytes = w4::gemm_workspace_bytes(a);
+      break;
+    }
     default: return fail(W4_ERR_INVALID, "op = %d is unknown", op);
   }
   return ok();
@@ -184,8 +191,6 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
 int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
              const w4_desc* desc, int transposed, const float* bias, float* Y, void* ws, size_t ws_bytes,
              void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int s = check_mm(A, M, packed, scales, zeros, desc, transposed, bias, Y);
   if (s != W4_OK) return s;
   if (M == 0) return ok();
@@ -195,7 +200,8 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   if (w4::gemm_lds_bytes(a) > device_lds_limit())
     return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a),
                 device_lds_limit());
-  return launched(w4::launch_gemm(a, st), "gemm");
+  if (ws != nullptr && !aligned(ws, 16)) return fail(W4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launched(w4::launch_gemm(a, ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
 }
 
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
@@ -208,7 +214,7 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, nullptr,
                                  nullptr);
   if (w4::gemv_supported(a, device_lds_limit())) return w4::gemv_name(a);
-  return w4::gemm_name(a);
+  return w4::gemm_name(a, true);
 }
 
 const char* w4_status_string(int status) {

@@ -27,6 +27,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <cstdio>
 #include <cstdlib>
 
 namespace w4 {
@@ -47,7 +48,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ scales,
                                                             const uint16_t* __restrict__ zeros,
                                                             const float* __restrict__ bias, float* __restrict__ Y,
-                                                            int M, int N, int K, int log2g) {
+                                                            int M, int N, int K, int log2g, int kt_per_slice,
+                                                            float* __restrict__ part) {
   constexpr int T = WM * WN * 64;
   constexpr int BM = WM * FM * 32;
   constexpr int BN = WN * FN * 32;
@@ -72,7 +74,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM;
   const int c0 = blockIdx.x * BN;
-  const int KT = (L + BK - 1) / BK;
+  // contraction steps of this workgroup: all of them, or one slice of a split-K launch
+  const int KT_ALL = (L + BK - 1) / BK;
+  const int KB = blockIdx.z * kt_per_slice;
+  const int KT = min(KT_ALL - KB, kt_per_slice);
 
   // ---- staging registers: one stage of raw global data (two buffers alternate)
   struct Regs {
@@ -88,7 +93,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   };
 
   auto load_stage = [&](int kt, Regs& R) {
-    const int l0 = kt * BK;
+    const int l0 = (KB + kt) * BK;
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;
       const int row = u / SLOTS, slot = u % SLOTS;
-      const bool in = TRANS ? kt * BK + slot * 8 < L : true;
+      const bool in = TRANS ? (KB + kt) * BK + slot * 8 < L : true;
       *reinterpret_cast<u32x4*>(as + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
     }
     if constexpr (!TRANS) {
@@ -275,22 +280,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   }
 
   // ---- epilogue: bias in fp32, masked fp32 stores.  Result register r of a 32x32
-  // block sits at row 8 (r / 4) + 4 (lane / 32) + (r % 4), column lane % 32.
+  // block sits at row 8 (r / 4) + 4 (lane / 32) + (r % 4), column lane % 32.  A split-K
+  // slice writes its partial sums (no bias) to its own [M][OUTC] plane of `part`.
+  float* out = part != nullptr ? part + (size_t)blockIdx.z * M * OUTC : Y;
+  const float* bz = part != nullptr ? nullptr : bias;
   const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
   const int cbase = c0 + wn * FN * 32 + lr;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = cbase + j * 32;
     if (c >= OUTC) continue;
-    const float b = bias != nullptr ? bias[c] : 0.0f;
+    const float b = bz != nullptr ? bz[c] : 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-        if (m < M) Y[(size_t)m * OUTC + c] = acc[i][j][r] + b;
+        if (m < M) out[(size_t)m * OUTC + c] = acc[i][j][r] + b;
       }
     }
+  }
+}
+
+// Split-K reduction: Y = sum over the S partial planes (fixed order) + bias.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t total,
+                                                            int outc, const float* __restrict__ bias,
+                                                            float* __restrict__ Y) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[(size_t)s * total + i];
+    if (bias != nullptr) v += bias[i % outc];
+    Y[i] = v;
   }
 }
 
@@ -318,32 +338,51 @@ constexpr Cfg kCfgs[] = {
 constexpr CfgEff kEff[] = {{1.0f, 1.0f}, {0.87f, 0.82f}, {0.64f, 0.64f}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
-int pick(const MmArgs& a) {
-  // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
+struct Plan {
+  int cfg;
+  int splits;
+};
+
+// Choose the tile configuration and the split-K factor.  score = full-tile efficiency x
+// how well the workgroups fill the 256 CUs in whole waves x how much of the edge tiles is
+// real work / (1 + the cost of writing and re-reading the split-K partial sums).
+Plan pick_plan(const MmArgs& a, bool allow_split) {
   static const int forced = [] {
+    // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
     const char* e = getenv("W4A16_GEMM_CFG");
     return e != nullptr ? atoi(e) : -1;
   }();
-  if (forced >= 0 && forced < kNumCfgs) return forced;
-  // score = full-tile efficiency x how well the tiles fill the 256 CUs in whole waves
-  // x how much of the edge tiles is real work
   const int64_t outc = a.transposed ? a.K : a.N;
-  int best = kNumCfgs - 1;
+  const int64_t L = a.transposed ? a.N : a.K;
+  Plan best{kNumCfgs - 1, 1};
   float best_score = -1.0f;
   for (int i = 0; i < kNumCfgs; ++i) {
+    if (forced >= 0 && forced < kNumCfgs && i != forced) continue;
     const Cfg& c = kCfgs[i];
     const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
     const int64_t tm = (a.M + bm - 1) / bm, tn = (outc + bn - 1) / bn;
-    const int64_t tiles = tm * tn;
-    const float waves = (float)((tiles + 255) / 256);
-    const float fill = (float)tiles / (256.0f * waves) * (float)a.M / (float)(tm * bm) * (float)outc / (float)(tn * bn);
-    const float score = fill * (a.transposed ? kEff[i].t : kEff[i].nt);
-    if (score > best_score) {
-      best_score = score;
-      best = i;
+    const int64_t kt = (L + c.bk - 1) / c.bk;
+    for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
+      if (sp > 1 && kt / sp < 16) break;  // keep >= 16 contraction steps per slice
+      const int64_t wgs = tm * tn * sp;
+      const float waves = (float)((wgs + 255) / 256);
+      const float fill = (float)wgs / (256.0f * waves) * (float)a.M / (float)(tm * bm) *
+                         (float)outc / (float)(tn * bn);
+      // partial planes: sp writes + sp reads of M x outc fp32 against 2 M outc L flops
+      const float over = sp > 1 ? 480.0f * (float)sp / (float)L : 0.0f;
+      const float score = fill * (a.transposed ? kEff[i].t : kEff[i].nt) / (1.0f + over);
+      if (score > best_score) {
+        best_score = score;
+        best = Plan{i, sp};
+      }
     }
   }
   return best;
+}
+
+size_t split_bytes(const MmArgs& a, const Plan& p) {
+  const int64_t outc = a.transposed ? a.K : a.N;
+  return p.splits > 1 ? (size_t)p.splits * a.M * outc * sizeof(float) : 0;
 }
 
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
@@ -353,7 +392,7 @@ size_t lds_bytes(const Cfg& c) {
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
-hipError_t run(const MmArgs& a, hipStream_t st) {
+hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
   constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
   // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
@@ -367,42 +406,61 @@ hipError_t run(const MmArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const int64_t outc = TRANS ? a.K : a.N;
-  const dim3 grid((unsigned)((outc + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
+  const int64_t L = TRANS ? a.N : a.K;
+  const int kt_all = (int)((L + BK - 1) / BK);
+  const int kts = (kt_all + splits - 1) / splits;
+  splits = (kt_all + kts - 1) / kts;  // every slice gets at least one contraction step
+  const dim3 grid((unsigned)((outc + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
   const int log2g = 31 - __builtin_clz((unsigned)a.group);
   k<<<grid, WM * WN * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.M, (int)a.N, (int)a.K,
-                                      log2g);
+                                      log2g, kts, splits > 1 ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total = a.M * outc;
+  const int64_t blocks = (total + 255) / 256;
+  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, total, (int)outc,
+                                                                                  a.bias, a.Y);
   return hipGetLastError();
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>
-hipError_t run_meta(const MmArgs& a, hipStream_t st) {
+hipError_t run_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
   switch (meta_kind(a.mode)) {
-    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GLOBAL>(a, st);
-    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_ROW>(a, st);
-    default: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GROUP>(a, st);
+    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GLOBAL>(a, splits, part, st);
+    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_ROW>(a, splits, part, st);
+    default: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GROUP>(a, splits, part, st);
   }
 }
 
 template <bool TRANS>
-hipError_t run_cfg(const MmArgs& a, hipStream_t st) {
-  switch (pick(a)) {
-    case 0: return run_meta<TRANS, 2, 2, 4, 4, 64, 2>(a, st);
-    case 1: return run_meta<TRANS, 4, 2, 2, 2, 64, 2>(a, st);
-    default: return run_meta<TRANS, 2, 2, 2, 2, 32, 3>(a, st);
+hipError_t run_cfg(const MmArgs& a, const Plan& p, float* part, hipStream_t st) {
+  switch (p.cfg) {
+    case 0: return run_meta<TRANS, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
+    case 1: return run_meta<TRANS, 4, 2, 2, 2, 64, 2>(a, p.splits, part, st);
+    default: return run_meta<TRANS, 2, 2, 2, 2, 32, 3>(a, p.splits, part, st);
   }
 }
 
 }  // namespace
 
-const char* gemm_name(const MmArgs& a) {
-  const Cfg& c = kCfgs[pick(a)];
-  return a.transposed ? c.name_t : c.name_nt;
+const char* gemm_name(const MmArgs& a, bool with_workspace) {
+  static thread_local char buf[64];
+  const Plan p = pick_plan(a, with_workspace);
+  const Cfg& c = kCfgs[p.cfg];
+  if (p.splits == 1) return a.transposed ? c.name_t : c.name_nt;
+  snprintf(buf, sizeof(buf), "%s_splitk%d", a.transposed ? c.name_t : c.name_nt, p.splits);
+  return buf;
 }
 
-size_t gemm_lds_bytes(const MmArgs& a) { return lds_bytes(kCfgs[pick(a)]); }
+size_t gemm_lds_bytes(const MmArgs& a) { return lds_bytes(kCfgs[pick_plan(a, false).cfg]); }
 
-hipError_t launch_gemm(const MmArgs& a, hipStream_t st) {
-  return a.transposed ? run_cfg<true>(a, st) : run_cfg<false>(a, st);
+size_t gemm_workspace_bytes(const MmArgs& a) { return split_bytes(a, pick_plan(a, true)); }
+
+hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  Plan p = pick_plan(a, ws != nullptr);
+  if (p.splits > 1 && split_bytes(a, p) > ws_bytes) p = pick_plan(a, false);
+  float* part = static_cast<float*>(ws);
+  return a.transposed ? run_cfg<true>(a, p, part, st) : run_cfg<false>(a, p, part, st);
 }
 
 }  // namespace w4

@@ -37,8 +37,12 @@ bool gemv_supported(const MmArgs& a, size_t lds_limit);
 const char* gemv_name(const MmArgs& a);
 hipError_t launch_gemv(const MmArgs& a, hipStream_t st);
 
-const char* gemm_name(const MmArgs& a);
+// GEMM: kernel name (with a split-K suffix when a workspace would be used), LDS
+// footprint, the workspace the split-K plan wants (0 if none) and the launch, which
+// splits the contraction only when `ws` holds at least the planned bytes.
+const char* gemm_name(const MmArgs& a, bool with_workspace);
 size_t gemm_lds_bytes(const MmArgs& a);
-hipError_t launch_gemm(const MmArgs& a, hipStream_t st);
+size_t gemm_workspace_bytes(const MmArgs& a);
+hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace w4

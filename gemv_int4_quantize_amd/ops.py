@@ -158,8 +158,11 @@ def dequantize(qw: QuantizedWeight, dtype=torch.bfloat16) -> torch.Tensor:
 
 
 def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: torch.Tensor | None = None,
-       out: torch.Tensor | None = None) -> torch.Tensor:
-    """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias); fp32 output."""
+       out: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
+    """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias); fp32 output.
+
+    split_k lets a GEMM with few output tiles split its contraction over a workspace
+    (allocated here from torch's caching allocator; the sum order is fixed)."""
     a = _as_bf16(a)
     _need_cuda(a, qw.packed, bias, out)
     if a.dim() != 2 or not a.is_contiguous():
@@ -175,8 +178,14 @@ def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: tor
     elif out.shape != (M, outc) or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError("out must be a contiguous fp32 tensor of the output shape")
     desc = qw.desc()
+    op = _lib.OP_MM_T if transposed else _lib.OP_MM
+    ws_bytes = ctypes.c_size_t(0)
+    if split_k:
+        check(lib().w4_workspace_bytes(ctypes.byref(desc), op, M, ctypes.byref(ws_bytes)))
+    ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=a.device) if ws_bytes.value else None
     check(lib().w4a16_mm(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
-                         1 if transposed else 0, _ptr(bias), _ptr(out), None, 0, _stream(a.device)))
+                         1 if transposed else 0, _ptr(bias), _ptr(out), _ptr(ws), ws_bytes.value,
+                         _stream(a.device)))
     return out
 
 

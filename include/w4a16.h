@@ -77,7 +77,11 @@ typedef struct {
 int w4_meta_pairs(const w4_desc* desc, int64_t* pairs);
 
 /* Device workspace, in bytes, that `op` needs for this descriptor (0 if none);
- * M is the activation row count for the matmul ops.  Host only. */
+ * M is the activation row count for the matmul ops.  For W4_OP_MM / W4_OP_MM_T
+ * a nonzero size is optional: it is the fp32 scratch of a split-K GEMM
+ * (S partial [M][out] planes, summed in a fixed order, so results stay
+ * deterministic), which the library plans when the output has too few tiles to
+ * fill the device.  Host only. */
 int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes);
 
 /* Quantize and pack W [N][K] (dtype w_dtype) into packed [N][K/8] int32 and the
@@ -105,7 +109,10 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
  * required (W4_ERR_UNSUPPORTED otherwise).  A and packed must be 16-byte
  * aligned, Y and bias 4-byte aligned.  M <= 4 non-transposed runs the
  * memory-bound GEMV (no matrix cores); other shapes run the MFMA GEMM.  ws may
- * be NULL when w4_workspace_bytes reports 0.  Sources: Objective 2 of
+ * always be NULL: the GEMM then runs unsplit.  A workspace of at least the
+ * bytes w4_workspace_bytes reports (16-byte aligned, owned by the caller, free
+ * to reuse once the stream has run the call) lets a GEMM with few output tiles
+ * split its contraction; a smaller one is ignored.  Sources: Objective 2 of
  * "Quantized LLM Inference with Triton Kernels"; "Re-write HQQ Fused Gemm
  * Transpose"; "[Kernel] Adding bias epilogue support for cutlass_scaled_mm";
  * "Modify small-batched weight only quantization". */
@@ -114,7 +121,8 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
              float* Y, void* ws, size_t ws_bytes, void* stream);
 
 /* Name of the kernel w4a16_mm would launch for these arguments ("gemv_m4",
- * "gemm_nt_256x128", ...), or NULL when they are invalid.  Host only. */
+ * "gemm_nt_256x128", "gemm_t_256x256_splitk4", ...) given the workspace
+ * w4_workspace_bytes reports, or NULL when they are invalid.  Host only. */
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed);
 
 /* Human-readable name of a status code. */

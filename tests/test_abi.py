@@ -72,6 +72,17 @@ def test_workspace_bytes():
     d = _lib.W4Desc(1024, 2048, _lib.MODE_GROUPWISE, 128)
     assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_QUANTIZE, 0, ctypes.byref(b)) == 0 and b.value == 0
     assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM, 4, ctypes.byref(b)) == 0 and b.value == 0
+    # a GEMM with few output tiles plans a split-K over fp32 partial planes [S][M][out]
+    d = _lib.W4Desc(4096, 4096, _lib.MODE_GROUPWISE, 128)
+    for op, name in ((_lib.OP_MM, "gemm_nt_"), (_lib.OP_MM_T, "gemm_t_")):
+        assert L.w4_workspace_bytes(ctypes.byref(d), op, 64, ctypes.byref(b)) == 0
+        k = w4.kernel_for(64, 4096, 4096, "groupwise", 128, transposed=op == _lib.OP_MM_T)
+        assert k.startswith(name) and "_splitk" in k
+        S = int(k.rsplit("_splitk", 1)[1])
+        assert S >= 2 and b.value == S * 64 * 4096 * 4
+        # enough output tiles: no split, no workspace
+        assert L.w4_workspace_bytes(ctypes.byref(d), op, 8192, ctypes.byref(b)) == 0 and b.value == 0
+        assert "_splitk" not in w4.kernel_for(8192, 4096, 4096, "groupwise", 128, transposed=op == _lib.OP_MM_T)
     assert L.w4_workspace_bytes(ctypes.byref(d), 99, 4, ctypes.byref(b)) == _lib.W4_ERR_INVALID
 
 
