@@ -63,19 +63,22 @@ int64_t pairs_of(const w4_desc* d) {
   return d->N * (d->K / d->group);
 }
 
-size_t device_lds_limit() {
-  static std::atomic<long long> cached{-1};
-  long long v = cached.load();
-  if (v < 0) {
-    int dev = 0, bytes = 0;
+w4::DeviceCaps device_caps() {
+  // queried once per process (one device type); defaults are MI355X's
+  static std::atomic<long long> lds{-1}, cus{-1};
+  if (lds.load() < 0) {
+    int dev = 0, bytes = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
       bytes = 64 * 1024;
-    v = bytes;
-    cached.store(v);
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus.store(n);
+    lds.store(bytes);
   }
-  return (size_t)v;
+  return w4::DeviceCaps{(size_t)lds.load(), (int)cus.load()};
 }
+
+size_t device_lds_limit() { return device_caps().lds; }
 
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -143,7 +146,7 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
       static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
       const w4::MmArgs a = make_args(dummy, M, reinterpret_cast<const int32_t*>(dummy), dummy, dummy, desc,
                                      op == W4_OP_MM_T, nullptr, nullptr);
-      if (!w4::gemv_supported(a, device_lds_limit())) *bytes = w4::gemm_workspace_bytes(a);
+      if (!w4::gemv_supported(a, device_caps())) *bytes = w4::gemm_workspace_bytes(a);
       break;
     }
     default: return fail(W4_ERR_INVALID, "op = %d is unknown", op);
@@ -196,7 +199,7 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   if (M == 0) return ok();
   const w4::MmArgs a = make_args(A, M, packed, scales, zeros, desc, transposed, bias, Y);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (w4::gemv_supported(a, device_lds_limit())) return launched(w4::launch_gemv(a, st), "gemv");
+  if (w4::gemv_supported(a, device_caps())) return launched(w4::launch_gemv(a, device_caps(), st), "gemv");
   if (w4::gemm_lds_bytes(a) > device_lds_limit())
     return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a),
                 device_lds_limit());
@@ -213,7 +216,7 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   if (s != W4_OK || M == 0) return nullptr;
   const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, nullptr,
                                  nullptr);
-  if (w4::gemv_supported(a, device_lds_limit())) return w4::gemv_name(a);
+  if (w4::gemv_supported(a, device_caps())) return w4::gemv_name(a);
   return w4::gemm_name(a, true);
 }
 

@@ -4,130 +4,174 @@
 // Design ("Modify small-batched weight only quantization", TensorRT-LLM #2213, names
 // load stalls and duplicate scale / zero requests as the costs of this kernel; here
 // on gfx950 with no matrix cores):
-//   * each wave owns R rows over the full K (split-K inside the wave, no partial
-//     results leave the wave); lane l streams 16-byte chunks c = l, l+64, ... of
-//     every row (32 codes each), so one wave-wide load is 1 KB contiguous;
-//   * X streams through two LDS windows of 2048 columns ([m][word][chunk], so that
-//     consecutive lanes read consecutive 16-byte slots, free of bank conflicts); the
-//     block refills one window while it computes on the other, so the LDS footprint
-//     (8 KB per activation row) does not grow with K;
-//   * the scale / zero bits of a chunk's group are loaded with the chunk, one
-//     iteration ahead (the lanes that share a group issue the same address inside one
-//     wave-wide load, which the memory pipeline merges into one request);
+//   * one workgroup (16 waves) per contiguous block of rows, about one block per CU:
+//     X is staged into LDS once per workgroup (in phases of up to PW x 2048 columns
+//     when M*K does not fit), so activation traffic does not grow with N;
+//   * each wave streams row groups of R rows over K; lane l owns the 16-byte chunk
+//     c = it*64 + l of a row (32 codes), so one wave-wide load is 1 KB contiguous;
+//   * weights, scales and zeros come in through buffer loads whose per-lane offset
+//     is fixed and whose row base is a scalar resource: no per-chunk address
+//     arithmetic, and rows / groups past the end read as zero (no bounds branches);
+//   * a two-slot register pipeline runs over the flattened (row group, iteration)
+//     steps of a wave, so the next row's loads are in flight while a row finishes;
 //   * dequantization is v_fma_mix_f32 on nibbles masked into fp16 halves, bf16
 //     rounding by v_cvt_pk_bf16_f32, products by v_dot2_f32_bf16;
-//   * the R*M partial sums of a wave are reduced with a transposing butterfly, so
-//     every shuffle step halves the number of live values.
+//   * the R*M partial sums of a row group are reduced across the wave with a
+//     transposing butterfly on v_permlane32_swap / v_permlane16_swap and DPP row
+//     moves (no LDS round trips), parked in LDS, and written out coalesced with the
+//     bias at the end.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
-
 namespace w4 {
 
-// Lane l ends up holding the wave-wide sum of value (l >> (6 - log2 V)).
+namespace {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// dword 3 of a raw buffer resource on gfx9-class devices (32-bit data format)
+constexpr int kRsrcDword3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcDword3);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// One butterfly stage on partners lane ^ o: while more than one value is live, the lanes
+// with the partner bit set keep the upper half of the values and the others the lower
+// half (transposing); with one value left it is a plain sum.
 template <int V>
-__device__ __forceinline__ float transpose_reduce(float (&v)[V], int lane) {
-  int n = V;
+__device__ __forceinline__ void swap_stage32(float (&v)[V], int& n) {
+  if (n > 1) {
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    if (n > 1) {
-      const int half = n / 2;
-      const bool upper = (lane & o) != 0;
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) {
-        if (i < half) {
-          const float send = upper ? v[i] : v[i + half];
-          const float keep = upper ? v[i + half] : v[i];
-          v[i] = keep + __shfl_xor(send, o);
-        }
+    for (int i = 0; i < V / 2; ++i)
+      if (i < n / 2) {
+        // lanes 0..31 receive lane+32's first operand, lanes 32..63 lane-32's second
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + n / 2]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
       }
-      n = half;
-    } else {
-      v[0] += __shfl_xor(v[0], o);
-    }
+    n /= 2;
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
+}
+
+template <int V>
+__device__ __forceinline__ void swap_stage16(float (&v)[V], int& n) {
+  if (n > 1) {
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i)
+      if (i < n / 2) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + n / 2]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+    n /= 2;
+  } else {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+template <int CTRL, int BIT, int V>
+__device__ __forceinline__ void dpp_stage(float (&v)[V], int& n, int lane) {
+  if (n > 1) {
+    const bool up = (lane & BIT) != 0;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i)
+      if (i < n / 2) {
+        const float send = up ? v[i] : v[i + n / 2];
+        const float keep = up ? v[i + n / 2] : v[i];
+        v[i] = keep + dpp_move<CTRL>(send);
+      }
+    n /= 2;
+  } else {
+    v[0] += dpp_move<CTRL>(v[0]);
+  }
+}
+
+// Wave-wide reduction of V partial sums (V <= 16): lane l ends up holding the total of
+// value l >> (6 - log2 V).  Partners: lane ^ 32, lane ^ 16 (permlane swaps), lane ^ 15
+// (DPP row_mirror), lane ^ 7 (row_half_mirror), lane ^ 2 and lane ^ 1 (quad_perm).
+template <int V>
+__device__ __forceinline__ float wave_reduce(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 16 && (V & (V - 1)) == 0, "V is a power of two <= 16");
+  int n = V;
+  swap_stage32(v, n);
+  swap_stage16(v, n);
+  dpp_stage<0x140, 8>(v, n, lane);  // row_mirror
+  dpp_stage<0x141, 4>(v, n, lane);  // row_half_mirror
+  v[0] += dpp_move<0x4E>(v[0]);     // quad_perm [2,3,0,1]
+  v[0] += dpp_move<0xB1>(v[0]);     // quad_perm [1,0,3,2]
   return v[0];
 }
 
-// Per-lane state of one pipeline stage: the 16-byte chunk of every row and the
-// raw fp16 scale / zero bits of the group(s) it belongs to (GPC groups per chunk).
+// Per-lane state of one pipeline step: the 16-byte chunk of each of R rows and the
+// fp16 scale / zero bits of the group(s) it belongs to (GPC groups per chunk).
 template <int R, int GPC>
 struct Stage {
   u32x4 w[R];
-  uint16_t s[R][GPC], z[R][GPC];  // kept 16-bit: v_fma_mix_f32 reads the low half as fp16
+  uint32_t s[R][GPC], z[R][GPC];  // zero-extended 16-bit loads; v_fma_mix_f32 reads the low half
 };
 
-template <int M, int R, int META, int WAVES, int GPC>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __restrict__ X,
-                                                          const int32_t* __restrict__ packed,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint16_t* __restrict__ zeros,
-                                                          const float* __restrict__ bias, float* __restrict__ Y,
-                                                          int N, int K, int log2g) {
-  // Two LDS windows of X, each [m][word][chunk] over the 2048 columns of one iteration:
-  // the block refills one window while it computes on the other.
-  __shared__ u32x4 xwin[2][M * 4 * 64];
-  constexpr int T = WAVES * 64;
-  constexpr int XUNITS = M * 4 * 64;  // 16-byte units per window
-  const int KS = K >> 5;              // 16-byte chunks (32 codes) per row
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // the wave index is uniform: keep every row-dependent value in scalar registers
+constexpr int kWaves = 16;
+
+// meta_row: (scale, zero) pairs per row (K / g, 1 for ROWWISE, 0 for GLOBAL);
+// log2g: group shift (31 for ROWWISE / GLOBAL, so every column maps to pair 0 of its row).
+template <int M, int R, int GPC>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __restrict__ X,
+                                                           const int32_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* __restrict__ zeros,
+                                                           const float* __restrict__ bias, float* __restrict__ Y,
+                                                           int N, int K, int meta_row, int log2g, int rows_per_block,
+                                                           int phase_iters) {
+  extern __shared__ u32x4 smem[];
+  constexpr int T = kWaves * 64;
+  const int KS = K >> 5;               // 16-byte chunks per row
+  const int iters = (KS + 63) >> 6;    // 2048-column iterations per row
+  const int PW = phase_iters;          // iterations whose X is resident at a time
+  u32x4* xs = smem;                                             // [PW][M][4 words][64 chunks]
+  float* outs = reinterpret_cast<float*>(smem + PW * M * 256);  // [rows_per_block][M]
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int row0 = (blockIdx.x * WAVES + wave) * R;
-  const int iters = (KS + 63) >> 6;
-  const int gpr = META == META_GROUP ? K >> log2g : 1;
+  const int r0 = blockIdx.x * rows_per_block;
+  const int r1 = min(r0 + rows_per_block, N);
   const int KW = K >> 3;
+  const uint32_t meta_bytes = meta_row > 0 ? (uint32_t)meta_row * 2 : 2u;
+  // row groups rg = wave, wave + 16, ... of R rows each
+  const int nrg = (r1 - r0 + R - 1) / R;
+  const int my_rg = nrg > wave ? (nrg - wave + kWaves - 1) / kWaves : 0;
 
-  const u32x4* prow[R];
-  const uint16_t* srow[R];
-  const uint16_t* zrow[R];
+  const uint32_t vo = lane * 16;
+  uint32_t vs[GPC];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int n = min(row0 + r, N - 1);
-    prow[r] = reinterpret_cast<const u32x4*>(packed + (size_t)n * KW);
-    srow[r] = scales + (size_t)n * gpr;
-    zrow[r] = zeros + (size_t)n * gpr;
-  }
+  for (int q = 0; q < GPC; ++q) vs[q] = ((uint32_t)(lane * 32 + q * 16) >> log2g) * 2;
 
-  // X units this thread moves into a window: unit u = (m * 64 + chunk) * 4 + word
-  constexpr int XPT = (XUNITS + T - 1) / T;
-  u32x4 xr[XPT];
-  auto xload = [&](int it) {
+  // Loads of step (row group k, iteration it); a row group past this wave's last one, or
+  // a row past the block, gets a zero-sized resource and reads zeros without a request.
+  auto load = [&](int k, int it, Stage<R, GPC>& st) {
+    const int rg = wave + k * kWaves;
+    const uint32_t so = ((uint32_t)(it * 2048) >> log2g) * 2;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int u = tid + i * T;
-      if (u < XUNITS) {
-        const int m = u >> 8, c = ((u >> 2) & 63) + it * 64, w = u & 3;
-        xr[i] = c < KS ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + c * 32 + w * 8) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto xstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int u = tid + i * T;
-      if (u < XUNITS) {
-        const int m = u >> 8, c = (u >> 2) & 63, w = u & 3;
-        xwin[buf][(m * 4 + w) * 64 + c] = xr[i];
-      }
-    }
-  };
-
-  // weight stage of iteration `it`: one chunk per row and its scale / zero bits
-  auto load = [&](int it, Stage<R, GPC>& st) {
-    const int c = min(it * 64 + lane, KS - 1);
-#pragma unroll
-    for (int r = 0; r < R; ++r) st.w[r] = __builtin_nontemporal_load(prow[r] + c);
-    if constexpr (META == META_GROUP) {
+    for (int r = 0; r < R; ++r) {
+      const int row = r0 + rg * R + r;
+      const bool ok = k < my_rg && row < r1;
+      const int n = min(row, r1 - 1);
+      const rsrc_t pr = make_rsrc(packed + (size_t)n * KW, ok ? (uint32_t)KW * 4 : 0u);
+      const rsrc_t sr = make_rsrc(scales + (size_t)n * meta_row, ok ? meta_bytes : 0u);
+      const rsrc_t zr = make_rsrc(zeros + (size_t)n * meta_row, ok ? meta_bytes : 0u);
+      st.w[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, vo + it * 1024, 0, 0));
 #pragma unroll
       for (int q = 0; q < GPC; ++q) {
-        const int G = (c * 32 + q * 16) >> log2g;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          st.s[r][q] = srow[r][G];
-          st.z[r][q] = zrow[r][G];
-        }
+        st.s[r][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[q] + so, 0, 0);
+        st.z[r][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, vs[q] + so, 0, 0);
       }
     }
   };
@@ -138,152 +182,163 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const uint16_t* __rest
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-  DqConst rc[R];
-  auto compute = [&](int it, const Stage<R, GPC>& st, int buf) {
-    if (it * 64 + lane >= KS) return;
-    DqConst dc[R][GPC];
-    if constexpr (META == META_GROUP) {
+  Stage<R, GPC> A, B;
+  for (int p0 = 0; p0 < iters; p0 += PW) {
+    const int pw = min(PW, iters - p0);
+    const int steps = my_rg * pw;
+    // step t of this phase -> (row group k = t / pw, iteration p0 + t % pw)
+    int lk = 0, lit = 0, ck = 0, cit = 0;
+    auto advance = [&](int& k, int& it) {
+      if (++it == pw) {
+        it = 0;
+        ++k;
+      }
+    };
+    load(lk, p0 + lit, A);
+    advance(lk, lit);
+
+    // X columns of this phase -> LDS, zero beyond K
+    if (p0 > 0) __syncthreads();  // every wave is done with the previous phase's X
+    const int units = pw * M * 256;
+    for (int u = tid; u < units; u += T) {
+      const int c = u & 63, w = (u >> 6) & 3, mi = u >> 8;
+      const int il = mi / M, m = mi - il * M;
+      const int col = ((p0 + il) * 64 + c) * 32 + w * 8;
+      xs[u] = col < K ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+
+    auto compute = [&](const Stage<R, GPC>& st) {
+      DqConst dc[R][GPC];
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int q = 0; q < GPC; ++q) dc[r][q] = dq_const_mix(st.s[r][q], st.z[r][q]);
-    }
+        for (int q = 0; q < GPC; ++q) dc[r][q] = dq_const_mix((uint16_t)st.s[r][q], (uint16_t)st.z[r][q]);
+      const u32x4* xb = xs + cit * M * 256 + lane;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x4 xv[M];
+      for (int w = 0; w < 4; ++w) {
+        u32x4 xv[M];
 #pragma unroll
-      for (int m = 0; m < M; ++m) xv[m] = xwin[buf][(m * 4 + w) * 64 + lane];
+        for (int m = 0; m < M; ++m) xv[m] = xb[(m * 4 + w) * 64];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        uint32_t bw[4];
-        if constexpr (META == META_GROUP)
+        for (int r = 0; r < R; ++r) {
+          uint32_t bw[4];
           dq_word_bf16(st.w[r][w], dc[r][GPC == 2 ? w / 2 : 0], bw);
-        else
-          dq_word_bf16(st.w[r][w], rc[r], bw);
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+          for (int m = 0; m < M; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[r][m] = dot2_bf16(bw[i], xv[m][i], acc[r][m]);
+            for (int i = 0; i < 4; ++i) acc[r][m] = dot2_bf16(bw[i], xv[m][i], acc[r][m]);
+        }
       }
-    }
-  };
-
-  Stage<R, GPC> A, B;
-  xload(0);
-  load(0, A);
-  if constexpr (META != META_GROUP) {
+      if (cit == pw - 1) {
+        // this phase of the row group is done: reduce across the wave, accumulate in LDS
+        constexpr int MP = M == 3 ? 4 : M;
+        constexpr int V = R * MP;
+        constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : 4;
+        float v[V];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int mi = META == META_GLOBAL ? 0 : min(row0 + r, N - 1);
-      rc[r] = dq_const_mix(scales[mi], zeros[mi]);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int m = 0; m < MP; ++m) v[r * MP + m] = m < M ? acc[r][m] : 0.0f;
+        const float sum = wave_reduce<V>(v, lane);
+        constexpr int SPAN = 64 / V;
+        const int idx = lane >> (6 - LOGV);
+        const int r = idx / MP, m = idx - (idx / MP) * MP;
+        const int lr = (wave + ck * kWaves) * R + r;  // row within the block
+        if ((lane & (SPAN - 1)) == 0 && m < M && r0 + lr < r1) {
+          float* o = outs + lr * M + m;  // each (row, m) belongs to one wave: no race
+          *o = p0 == 0 ? sum : *o + sum;
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+          for (int mm = 0; mm < M; ++mm) acc[rr][mm] = 0.0f;
+      }
+      advance(ck, cit);
+    };
+
+    // two slots, unrolled by two: the slot being filled is never the one being read,
+    // and every iteration issues exactly one step of loads (exact wait counts)
+    int t = 0;
+    for (; t + 2 <= steps; t += 2) {
+      load(lk, p0 + lit, B);
+      advance(lk, lit);
+      compute(A);
+      load(lk, p0 + lit, A);
+      advance(lk, lit);
+      compute(B);
     }
+    if (t < steps) compute(A);
   }
-  xstore(0);
+
   __syncthreads();
-
-  // Two register stages, unrolled by two so the in-flight stage is never copied.  The
-  // next X window is requested before the next weight stage, so storing it to LDS never
-  // waits for the weights; the loop body issues exactly one weight stage while consuming
-  // the other (no conditional loads), and the tail is peeled.
-  int it = 0;
-  for (; it + 2 < iters; it += 2) {
-    xload(it + 1);
-    load(it + 1, B);
-    compute(it, A, 0);
-    xstore(1);
-    __syncthreads();
-    xload(it + 2);
-    load(it + 2, A);
-    compute(it + 1, B, 1);
-    xstore(0);
-    __syncthreads();
-  }
-  if (it + 1 < iters) {
-    xload(it + 1);
-    load(it + 1, B);
-    compute(it, A, 0);
-    xstore(1);
-    __syncthreads();
-    compute(it + 1, B, 1);
-  } else {
-    compute(it, A, 0);
-  }
-
-  // reduce R x MP partial sums across the wave (MP = M padded to a power of two)
-  constexpr int MP = M == 3 ? 4 : M;
-  constexpr int V = R * MP;
-  float v[V];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < MP; ++m) v[r * MP + m] = m < M ? acc[r][m] : 0.0f;
-  constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : V == 16 ? 4 : 5;
-  const float sum = transpose_reduce<V>(v, lane);
-  constexpr int SPAN = 64 / V;
-  if ((lane & (SPAN - 1)) == 0) {
-    const int idx = lane >> (6 - LOGV);
-    const int r = idx / MP, m = idx - (idx / MP) * MP;
-    const int n = row0 + r;
-    if (m < M && n < N) Y[(size_t)m * N + n] = sum + (bias != nullptr ? bias[n] : 0.0f);
+  for (int u = tid; u < (r1 - r0) * M; u += T) {
+    const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
+    const int n = r0 + lr;
+    Y[(size_t)m * N + n] = outs[lr * M + m] + (bias != nullptr ? bias[n] : 0.0f);
   }
 }
 
-// ---------------------------------------------------------------- host side
-
-namespace {
-
 struct GemvPlan {
-  int R, waves;
+  int R;
+  int blocks, rows_per_block;
+  int phase_iters;
   size_t lds;
 };
 
-int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
-
-GemvPlan plan(const MmArgs& a) {
-  // rows per wave and waves per block: keep >= 256 blocks (one per CU) in flight
+GemvPlan plan(const MmArgs& a, const DeviceCaps& caps) {
   GemvPlan p;
-  p.waves = 8;
-  p.R = a.N >= 16 * 512 ? 2 : 1;
-  if (a.N < 8 * 256) p.waves = 4;
-  p.lds = (size_t)2 * a.M * 4 * 64 * 16;
+  const int iters = (int)((a.K / 32 + 63) / 64);
+  const size_t x_iter = (size_t)a.M * 4096;  // LDS bytes of X per 2048-column iteration
+  // Tall weights: two rows per wave halve the X reads from LDS; one block per CU.
+  // Otherwise one row per wave and two blocks per CU when the LDS allows it.
+  p.R = a.N >= 16384 ? 2 : 1;
+  const int per_cu = p.R == 1 && (size_t)iters * x_iter <= 72 * 1024 ? 2 : 1;
+  p.blocks = caps.cus * per_cu;
+  p.rows_per_block = (int)((a.N + p.blocks - 1) / p.blocks);
+  if (p.rows_per_block > 1024) p.rows_per_block = 1024;
+  p.blocks = (int)((a.N + p.rows_per_block - 1) / p.rows_per_block);
+  const size_t outs = (size_t)p.rows_per_block * a.M * 4;
+  const size_t budget = caps.lds > outs ? caps.lds - outs : 0;
+  p.phase_iters = (int)std::min<size_t>((size_t)iters, budget / x_iter);
+  p.lds = (size_t)p.phase_iters * x_iter + outs;
   return p;
 }
 
-template <int M, int R, int META, int WAVES>
+int meta_row(const MmArgs& a) {
+  if (a.mode == W4_MODE_GLOBAL) return 0;
+  if (a.mode == W4_MODE_ROWWISE) return 1;
+  return (int)(a.K / a.group);
+}
+
+template <int M, int R, int GPC>
 hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  auto k = (META == META_GROUP && a.group == 16) ? gemv_kernel<M, R, META, WAVES, 2> : gemv_kernel<M, R, META, WAVES, 1>;
-  const int rows_per_block = R * WAVES;
-  const dim3 grid((unsigned)((a.N + rows_per_block - 1) / rows_per_block));
-  const int log2g = 31 - __builtin_clz((unsigned)a.group);  // GROUPWISE g is a power of two
-  k<<<grid, WAVES * 64, 0, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.N, (int)a.K, log2g);
+  auto k = gemv_kernel<M, R, GPC>;
+  static std::atomic<int> lds_set{64 * 1024};  // largest dynamic LDS size enabled so far
+  if ((int)p.lds > lds_set.load()) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
+    if (e != hipSuccess) return e;
+    lds_set.store((int)p.lds);
+  }
+  const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
+  k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.N, (int)a.K,
+                                           meta_row(a), log2g, p.rows_per_block, p.phase_iters);
   return hipGetLastError();
 }
 
-template <int M, int R, int META>
-hipError_t run_w(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  return p.waves == 4 ? run<M, R, META, 4>(a, p, st) : run<M, R, META, 8>(a, p, st);
-}
-
-template <int M, int META>
-hipError_t run_r(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  return p.R == 2 ? run_w<M, 2, META>(a, p, st) : run_w<M, 1, META>(a, p, st);
-}
-
 template <int M>
-hipError_t run_meta(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  switch (meta_kind(a.mode)) {
-    case META_GLOBAL: return run_r<M, META_GLOBAL>(a, p, st);
-    case META_ROW: return run_r<M, META_ROW>(a, p, st);
-    default: return run_r<M, META_GROUP>(a, p, st);
-  }
+hipError_t run_m(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
+  const bool g16 = a.mode == W4_MODE_GROUPWISE && a.group == 16;  // two groups per 32-code chunk
+  if (p.R == 2) return g16 ? run<M, 2, 2>(a, p, st) : run<M, 2, 1>(a, p, st);
+  return g16 ? run<M, 1, 2>(a, p, st) : run<M, 1, 1>(a, p, st);
 }
 
 }  // namespace
 
-bool gemv_supported(const MmArgs& a, size_t lds_limit) {
+bool gemv_supported(const MmArgs& a, const DeviceCaps& caps) {
   if (a.transposed || a.M < 1 || a.M > 4) return false;
   if (a.N > (int64_t)1 << 30 || a.K > (int64_t)1 << 30) return false;
-  return plan(a).lds <= lds_limit;
+  return plan(a, caps).phase_iters >= 1;
 }
 
 const char* gemv_name(const MmArgs& a) {
@@ -291,13 +346,13 @@ const char* gemv_name(const MmArgs& a) {
   return names[a.M - 1];
 }
 
-hipError_t launch_gemv(const MmArgs& a, hipStream_t st) {
-  const GemvPlan p = plan(a);
+hipError_t launch_gemv(const MmArgs& a, const DeviceCaps& caps, hipStream_t st) {
+  const GemvPlan p = plan(a, caps);
   switch (a.M) {
-    case 1: return run_meta<1>(a, p, st);
-    case 2: return run_meta<2>(a, p, st);
-    case 3: return run_meta<3>(a, p, st);
-    default: return run_meta<4>(a, p, st);
+    case 1: return run_m<1>(a, p, st);
+    case 2: return run_m<2>(a, p, st);
+    case 3: return run_m<3>(a, p, st);
+    default: return run_m<4>(a, p, st);
   }
 }
 

@@ -31,11 +31,17 @@ struct MmArgs {
   bool transposed;
 };
 
+// Properties of the current device that kernel plans depend on.
+struct DeviceCaps {
+  size_t lds;  // dynamic LDS bytes one workgroup may use
+  int cus;     // compute units
+};
+
 // GEMV (M <= 4, non-transposed).  Returns false if this shape cannot run on it
 // (LDS footprint), so the caller can fall back to the GEMM.
-bool gemv_supported(const MmArgs& a, size_t lds_limit);
+bool gemv_supported(const MmArgs& a, const DeviceCaps& caps);
 const char* gemv_name(const MmArgs& a);
-hipError_t launch_gemv(const MmArgs& a, hipStream_t st);
+hipError_t launch_gemv(const MmArgs& a, const DeviceCaps& caps, hipStream_t st);
 
 // GEMM: kernel name (with a split-K suffix when a workspace would be used), LDS
 // footprint, the workspace the split-K plan wants (0 if none) and the launch, which

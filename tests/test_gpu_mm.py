@@ -44,6 +44,21 @@ def test_gemv_small(M, mode, g, N, K):
     assert_mm_close(host(y), O.matmul(x, *ref, K, bias=bias), f"gemv M={M} {mode}{g}")
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("mode,g", [("groupwise", 128), ("rowwise", None), ("groupwise", 16)],
+                         ids=["groupwise128", "rowwise", "groupwise16"])
+def test_gemv_long_k(M, mode, g):
+    """K long enough that X is staged into LDS in several phases (K = 47104 + 1024 ragged)."""
+    N, K = 300, 48128
+    print(f"[case] gemv long K M={M} N={N} K={K} mode={mode} g={g}", flush=True)
+    _, ref, qw = _setup(707, M, N, K, mode, g)
+    x = synth.activations_bf16(707, M, M, K)
+    bias = synth.bias_f32(707, M, N)
+    assert w4.kernel_for(M, N, K, mode, g) == f"gemv_m{M}"
+    y = w4.mm(dev_bf16(x), qw, bias=dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(x, *ref, K, bias=bias), f"gemv long K M={M} {mode}{g}")
+
+
 GEMM_MODES = [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 64), ("groupwise", 256)]
 
 
