@@ -318,25 +318,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 namespace {
 
+// Tile configurations.  kind 0: the LDS-staged kernel above (both directions; the
+// non-transposed form only serves contractions too long for the register-operand kernel);
+// kind 1 / 2: the non-transposed register-operand kernel (gemm_nt.hip) with 128 x 128 /
+// 256 x 128 tiles.  `eff`: throughput of a full tile relative to the best of its
+// direction, measured on MI355X at the fine-tune shapes.
 struct Cfg {
+  int kind;
   int wm, wn, fm, fn, bk, stages;
-  const char* name_nt;
-  const char* name_t;
-};
-
-// wave tile (fm x 32) x (fn x 32), block tile (wm * fm * 32) x (wn * fn * 32)
-// Tile configurations.  `eff_nt` / `eff_t`: throughput of a full tile relative to the
-// best one, measured on MI355X at the fine-tune shapes (M = 4096, groupwise g = 64).
-struct CfgEff {
-  float nt, t;
+  const char* name;
+  bool transposed;
+  float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {2, 2, 4, 4, 64, 2, "gemm_nt_256x256", "gemm_t_256x256"},
-    {4, 2, 2, 2, 64, 2, "gemm_nt_256x128", "gemm_t_256x128"},
-    {2, 2, 2, 2, 32, 3, "gemm_nt_128x128", "gemm_t_128x128"},
+    {0, 2, 2, 4, 4, 64, 2, "gemm_t_256x256", true, 1.0f},
+    {0, 4, 2, 2, 2, 64, 2, "gemm_t_256x128", true, 0.82f},
+    {0, 2, 2, 2, 2, 32, 3, "gemm_t_128x128", true, 0.64f},
+    {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 1.0f},
+    {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 0.96f},
+    {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 0.7f},
 };
-constexpr CfgEff kEff[] = {{1.0f, 1.0f}, {0.87f, 0.82f}, {0.64f, 0.64f}};
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+constexpr int kNtLdsCfg = 5;
 
 struct Plan {
   int cfg;
@@ -344,7 +347,7 @@ struct Plan {
 };
 
 // Choose the tile configuration and the split-K factor.  score = full-tile efficiency x
-// how well the workgroups fill the 256 CUs in whole waves x how much of the edge tiles is
+// how well the workgroups fill the CUs in whole waves x how much of the edge tiles is
 // real work / (1 + the cost of writing and re-reading the split-K partial sums).
 Plan pick_plan(const MmArgs& a, bool allow_split) {
   static const int forced = [] {
@@ -354,23 +357,28 @@ Plan pick_plan(const MmArgs& a, bool allow_split) {
   }();
   const int64_t outc = a.transposed ? a.K : a.N;
   const int64_t L = a.transposed ? a.N : a.K;
-  Plan best{kNumCfgs - 1, 1};
+  const bool reg_ok = gemm_nt_reg_supported(a);
+  Plan best{a.transposed ? 2 : (reg_ok ? 3 : kNtLdsCfg), 1};
   float best_score = -1.0f;
   for (int i = 0; i < kNumCfgs; ++i) {
-    if (forced >= 0 && forced < kNumCfgs && i != forced) continue;
     const Cfg& c = kCfgs[i];
+    if (c.transposed != a.transposed) continue;
+    if (!a.transposed && (c.kind != 0) != reg_ok) continue;
+    if (forced >= 0 && forced < kNumCfgs && kCfgs[forced].transposed == a.transposed && i != forced) continue;
+    // waves per workgroup times resident workgroups per CU, in units of one 256-thread group
     const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
     const int64_t tm = (a.M + bm - 1) / bm, tn = (outc + bn - 1) / bn;
     const int64_t kt = (L + c.bk - 1) / c.bk;
+    const int64_t slots = c.kind == 1 ? 3 * 256 : c.kind == 2 ? 2 * 256 : 256;  // resident workgroups
     for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
       if (sp > 1 && kt / sp < 16) break;  // keep >= 16 contraction steps per slice
       const int64_t wgs = tm * tn * sp;
-      const float waves = (float)((wgs + 255) / 256);
-      const float fill = (float)wgs / (256.0f * waves) * (float)a.M / (float)(tm * bm) *
+      const float waves = (float)((wgs + slots - 1) / slots);
+      const float fill = (float)wgs / ((float)slots * waves) * (float)a.M / (float)(tm * bm) *
                          (float)outc / (float)(tn * bn);
       // partial planes: sp writes + sp reads of M x outc fp32 against 2 M outc L flops
       const float over = sp > 1 ? 480.0f * (float)sp / (float)L : 0.0f;
-      const float score = fill * (a.transposed ? kEff[i].t : kEff[i].nt) / (1.0f + over);
+      const float score = fill * c.eff / (1.0f + over);
       if (score > best_score) {
         best_score = score;
         best = Plan{i, sp};
@@ -388,6 +396,7 @@ size_t split_bytes(const MmArgs& a, const Plan& p) {
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
 
 size_t lds_bytes(const Cfg& c) {
+  if (c.kind != 0) return (size_t)2 * c.fm * 32 * (c.bk + 8) * 2;  // two activation buffers
   return (size_t)c.stages * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
 }
 
@@ -416,11 +425,7 @@ hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
                                       log2g, kts, splits > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  const int64_t total = a.M * outc;
-  const int64_t blocks = (total + 255) / 256;
-  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, total, (int)outc,
-                                                                                  a.bias, a.Y);
-  return hipGetLastError();
+  return launch_splitk_reduce(part, splits, a.M * outc, (int)outc, a.bias, a.Y, st);
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>
@@ -432,23 +437,36 @@ hipError_t run_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
   }
 }
 
-template <bool TRANS>
-hipError_t run_cfg(const MmArgs& a, const Plan& p, float* part, hipStream_t st) {
-  switch (p.cfg) {
-    case 0: return run_meta<TRANS, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
-    case 1: return run_meta<TRANS, 4, 2, 2, 2, 64, 2>(a, p.splits, part, st);
-    default: return run_meta<TRANS, 2, 2, 2, 2, 32, 3>(a, p.splits, part, st);
+hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st) {
+  if (a.transposed) {
+    switch (p.cfg) {
+      case 0: return run_meta<true, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
+      case 1: return run_meta<true, 4, 2, 2, 2, 64, 2>(a, p.splits, part, st);
+      default: return run_meta<true, 2, 2, 2, 2, 32, 3>(a, p.splits, part, st);
+    }
+  }
+  switch (kCfgs[p.cfg].kind) {
+    case 1: return launch_gemm_nt_reg(a, 0, p.splits, part, st);
+    case 2: return launch_gemm_nt_reg(a, 1, p.splits, part, st);
+    default: return run_meta<false, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
   }
 }
 
 }  // namespace
 
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t total, int outc, const float* bias, float* Y,
+                                hipStream_t st) {
+  const int64_t blocks = (total + 255) / 256;
+  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, total, outc, bias, Y);
+  return hipGetLastError();
+}
+
 const char* gemm_name(const MmArgs& a, bool with_workspace) {
   static thread_local char buf[64];
   const Plan p = pick_plan(a, with_workspace);
   const Cfg& c = kCfgs[p.cfg];
-  if (p.splits == 1) return a.transposed ? c.name_t : c.name_nt;
-  snprintf(buf, sizeof(buf), "%s_splitk%d", a.transposed ? c.name_t : c.name_nt, p.splits);
+  if (p.splits == 1) return c.name;
+  snprintf(buf, sizeof(buf), "%s_splitk%d", c.name, p.splits);
   return buf;
 }
 
@@ -459,8 +477,7 @@ size_t gemm_workspace_bytes(const MmArgs& a) { return split_bytes(a, pick_plan(a
 hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
   Plan p = pick_plan(a, ws != nullptr);
   if (p.splits > 1 && split_bytes(a, p) > ws_bytes) p = pick_plan(a, false);
-  float* part = static_cast<float*>(ws);
-  return a.transposed ? run_cfg<true>(a, p, part, st) : run_cfg<false>(a, p, part, st);
+  return run_plan(a, p, static_cast<float*>(ws), st);
 }
 
 }  // namespace w4

@@ -1,0 +1,342 @@
+// Non-transposed MFMA W4A16 GEMM for gfx950 with the weight operand dequantized straight
+// into MFMA registers:  Y[m][n] = sum_k X[m][k] * w[n][k] (+ bias[n]),
+// w = bf16_rne((q - z) * s), bf16 MFMA operands, fp32 accumulation.
+// Sources: Objective 2 of "Quantized LLM Inference with Triton Kernels" (Y = X_bf16 @
+// W_int4^T); "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560).
+//
+// Why this shape on gfx950: the B operand of v_mfma_f32_32x32x16_bf16 is, per lane, eight
+// consecutive contraction values of one output column -- exactly one packed int32 word of
+// a weight row.  So each lane loads its own words (one dwordx4 = 32 contraction values of
+// one row per 64-wide step) and dequantizes them into operand registers; the weights never
+// pass through LDS.  Only the activation tile is staged in LDS (shared by the 4 waves).
+//   * workgroup = 4 waves side by side along N; wave w owns output columns
+//     [c0 + 32 FN w, +32 FN) and all BM = 32 FM rows of the tile;
+//   * within a 64-wide contraction step the contraction order is permuted: MFMA step kk,
+//     operand slot 8 h + t (h = lane / 32) is contraction index k0 + 32 h + 8 kk + t, so a
+//     lane's four words for the step are contiguous; the activation fragment is read from
+//     LDS with the same mapping;
+//   * activation tiles: global -> VGPR -> LDS (two buffers, rows padded by 16 bytes),
+//     loaded two steps ahead; weight words one step ahead; one barrier per step;
+//   * inside a step, the LDS fragments and the dequantized words of sub-step kk+1 are
+//     produced while the MFMAs of kk issue;
+//   * scale / zero: rowwise and global modes load them once; groupwise loads, once per
+//     two steps, the 128 / g groups those steps cover with one wide load per array (when
+//     K % 128 == 0, else one pair per step);
+//   * dequantization: v_fma_mix_f32 on nibbles masked into fp16 halves, then
+//     v_cvt_pk_bf16_f32 (17 VALU per word); with FM = 4 row blocks per wave that is about
+//     4 VALU per MFMA, which the matrix core mostly overlaps;
+//   * split-K: blockIdx.z takes a contiguous range of steps and writes fp32 partial sums
+//     to its own plane; a separate kernel sums the planes in a fixed order.
+#include "common.h"
+#include "launch.h"
+
+namespace w4 {
+
+namespace {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+constexpr int kRsrcDword3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 class)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcDword3);
+}
+
+constexpr int kBK = 64;   // contraction per step
+constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
+
+// META: 0 one (scale, zero) per row (rowwise / global), 1 groupwise with one wide load per
+// two steps, 2 groupwise with one pair per step.  GPW: groups per 32-value lane chunk
+// (2 when g = 16).  KTAIL: K % 64 != 0 (activation columns past K are zeroed in LDS).
+template <int FM, int FN, int GPW, int META, bool KTAIL>
+__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
+                                                         const int32_t* __restrict__ packed,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint16_t* __restrict__ zeros,
+                                                         const float* __restrict__ bias, float* __restrict__ Y,
+                                                         int M, int N, int K, int meta_row, int log2g,
+                                                         int kt_per_slice, float* __restrict__ part) {
+  constexpr int BM = FM * 32, BN = 4 * FN * 32;
+  constexpr int AU = BM * 8 / 256;  // 16-byte activation units per thread per step
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  uint16_t* As0 = smem;
+  uint16_t* As1 = smem + BM * kLR;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = blockIdx.y * BM, c0 = blockIdx.x * BN;
+  const int KT_ALL = (K + kBK - 1) / kBK;
+  const int KB = blockIdx.z * kt_per_slice;  // first step of this slice (even)
+  const int KT = min(KT_ALL - KB, kt_per_slice);
+  const int KW = K >> 3;
+
+  // activations: one resource over the tile's rows (rows past M read as zero)
+  const rsrc_t ar = make_rsrc(A + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  uint32_t a_off[AU];
+#pragma unroll
+  for (int i = 0; i < AU; ++i) {
+    const int u = tid + i * 256;
+    a_off[i] = (uint32_t)((u >> 3) * K * 2 + (u & 7) * 16);
+  }
+  // weights: this wave's 32 FN rows (rows past N read as zero)
+  const int n0w = c0 + wave * FN * 32;
+  const int rows_w = max(0, min(FN * 32, N - n0w));
+  const int nb = min(n0w, N - 1);
+  const rsrc_t br = make_rsrc(packed + (size_t)nb * KW, (uint32_t)(rows_w * KW * 4));
+  const uint32_t mbytes = meta_row > 0 ? (uint32_t)(rows_w * meta_row * 2) : (rows_w > 0 ? 2u : 0u);
+  const rsrc_t sr = make_rsrc(scales + (size_t)nb * meta_row, mbytes);
+  const rsrc_t zr = make_rsrc(zeros + (size_t)nb * meta_row, mbytes);
+  const int h = lane >> 5, lr = lane & 31;
+  uint32_t b_off[FN], mrow_off[FN], m_off[FN][GPW];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    b_off[j] = (uint32_t)((lr + j * 32) * KW * 4 + h * 16);
+    mrow_off[j] = (uint32_t)((lr + j * 32) * meta_row * 2);
+#pragma unroll
+    for (int q = 0; q < GPW; ++q) m_off[j][q] = mrow_off[j] + (((uint32_t)(h * 32 + q * 16) >> log2g) * 2);
+  }
+  // META 1: bytes of one wide load = 2 * max(1, 128 / g)
+  const int wide_bytes = (128 >> log2g) >= 1 ? (128 >> log2g) * 2 : 2;
+
+  struct ARegs {
+    u32x4 a[AU];
+  };
+  struct BRegs {
+    u32x4 w[FN];
+    uint32_t s[FN][GPW], z[FN][GPW];
+  };
+  struct MRegs {
+    u32x4 s[FN], z[FN];
+  };
+
+  auto load_a = [&](int kt, ARegs& R) {
+#pragma unroll
+    for (int i = 0; i < AU; ++i)
+      R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[i] + kt * kBK * 2, 0, 0));
+  };
+  auto load_b = [&](int kt, BRegs& R) {
+    const uint32_t mk = ((uint32_t)(kt * kBK) >> log2g) * 2;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, b_off[j] + kt * 32, 0, 0));
+      if constexpr (META == 2) {
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+          R.s[j][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, m_off[j][q] + mk, 0, 0);
+          R.z[j][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, m_off[j][q] + mk, 0, 0);
+        }
+      }
+    }
+  };
+  // groups of steps kt, kt + 1 (kt even): 128 / g consecutive pairs, aligned because
+  // K % 128 == 0 makes every row's group count a multiple of 128 / g
+  auto load_m = [&](int kt, MRegs& R) {
+    const uint32_t mk = ((uint32_t)(kt * kBK) >> log2g) * 2;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint32_t o = mrow_off[j] + mk;
+      if (wide_bytes == 16) {
+        R.s[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
+        R.z[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, o, 0, 0));
+      } else if (wide_bytes == 8) {
+        const u32x2v a = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, o, 0, 0));
+        const u32x2v b = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(zr, o, 0, 0));
+        R.s[j] = u32x4{a[0], a[1], 0u, 0u};
+        R.z[j] = u32x4{b[0], b[1], 0u, 0u};
+      } else if (wide_bytes == 4) {
+        R.s[j] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(sr, o, 0, 0), 0u, 0u, 0u};
+        R.z[j] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(zr, o, 0, 0), 0u, 0u, 0u};
+      } else {
+        R.s[j] = u32x4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sr, o, 0, 0), 0u, 0u, 0u};
+        R.z[j] = u32x4{(uint32_t)__builtin_amdgcn_raw_buffer_load_b16(zr, o, 0, 0), 0u, 0u, 0u};
+      }
+    }
+  };
+  auto half_of = [&](const u32x4& v, int e) -> uint16_t { return (uint16_t)(v[e >> 1] >> ((e & 1) * 16)); };
+  auto store_a = [&](int kt, const ARegs& R, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < AU; ++i) {
+      const int u = tid + i * 256;
+      u32x4 v = R.a[i];
+      // past K the weight words are another row's (finite) codes: the activations must be 0
+      if constexpr (KTAIL) {
+        if (kt * kBK + (u & 7) * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
+      }
+      *reinterpret_cast<u32x4*>(buf + (u >> 3) * kLR + (u & 7) * 8) = v;
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto dequant = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], int kk, bf16x8 (&bfr)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      uint32_t o[4];
+      dq_word_bf16(B.w[j][kk], dc[j][GPW == 2 ? kk / 2 : 0], o);
+      bfr[j] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+    }
+  };
+  auto read_a = [&](const uint16_t* buf, int kk, bf16x8 (&af)[FM]) {
+    const uint16_t* as = buf + lr * kLR + h * 32 + kk * 8;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * kLR);
+  };
+  auto compute = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], const uint16_t* buf) {
+    bf16x8 af[2][FM], bfr[2][FN];
+    read_a(buf, 0, af[0]);
+    dequant(B, dc, 0, bfr[0]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk & 1;
+      if (kk < 3) {
+        read_a(buf, kk + 1, af[c ^ 1]);
+        dequant(B, dc, kk + 1, bfr[c ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // dequantization constants of step p (0: kt, 1: kt + 1) from the wide meta registers:
+  // half index g=16: 4p + 2h + q; g=32: 2p + h; g=64: p; g>=128: 0
+  auto dc_wide = [&](const MRegs& R, int p, DqConst (&dc)[FN][GPW]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < GPW; ++q) {
+        const int e = GPW == 2 ? 4 * p + 2 * h + q : wide_bytes == 8 ? 2 * p + h : wide_bytes == 4 ? p : 0;
+        dc[j][q] = dq_const_mix(half_of(R.s[j], e), half_of(R.z[j], e));
+      }
+  };
+  auto dc_step = [&](const BRegs& B, DqConst (&dc)[FN][GPW]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < GPW; ++q) dc[j][q] = dq_const_mix((uint16_t)B.s[j][q], (uint16_t)B.z[j][q]);
+  };
+
+  ARegs A0, A1;
+  BRegs B0, B1;
+  MRegs MM;
+  DqConst dcA[FN][GPW], dcB[FN][GPW];
+  if constexpr (META == 0) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const uint16_t sv = __builtin_amdgcn_raw_buffer_load_b16(sr, mrow_off[j], 0, 0);
+      const uint16_t zv = __builtin_amdgcn_raw_buffer_load_b16(zr, mrow_off[j], 0, 0);
+      dcA[j][0] = dq_const_mix(sv, zv);
+      dcB[j][0] = dcA[j][0];
+    }
+  }
+  // steps KB + t; loads past the slice read other (finite) data or zeros and are never used
+  load_b(KB, B0);
+  if constexpr (META == 1) load_m(KB, MM);
+  load_a(KB, A0);
+  load_a(KB + min(1, KT - 1), A1);
+  store_a(KB, A0, As0);
+  __syncthreads();
+  int t = 0;
+  for (; t + 2 <= KT; t += 2) {
+    const int kt = KB + t;
+    load_b(kt + 1, B1);
+    load_a(kt + 2, A0);
+    store_a(kt + 1, A1, As1);
+    if constexpr (META == 1) {
+      dc_wide(MM, 0, dcA);
+      dc_wide(MM, 1, dcB);
+    } else if constexpr (META == 2) {
+      dc_step(B0, dcA);
+    }
+    compute(B0, dcA, As0);
+    __syncthreads();
+    load_b(kt + 2, B0);
+    if constexpr (META == 1) load_m(kt + 2, MM);
+    load_a(kt + 3, A1);
+    store_a(kt + 2, A0, As0);
+    if constexpr (META == 2) dc_step(B1, dcB);
+    compute(B1, dcB, As1);
+    __syncthreads();
+  }
+  if (t < KT) {
+    if constexpr (META == 1) dc_wide(MM, 0, dcA);
+    else if constexpr (META == 2) dc_step(B0, dcA);
+    compute(B0, dcA, As0);
+  }
+
+  // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
+  // lr; a split-K slice writes its partial sums (no bias) to its own [M][N] plane
+  float* out = part != nullptr ? part + (size_t)blockIdx.z * M * N : Y;
+  const float* bz = part != nullptr ? nullptr : bias;
+  const int rbase = m0 + h * 4;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int c = n0w + j * 32 + lr;
+    if (c >= N) continue;
+    const float b = bz != nullptr ? bz[c] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
+        if (m < M) out[(size_t)m * N + c] = acc[i][j][r] + b;
+      }
+  }
+}
+
+template <int FM, int FN, int GPW, int META, bool KTAIL>
+hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) {
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL>;
+  constexpr int BM = FM * 32, BN = 4 * FN * 32;
+  const int lds = 2 * BM * kLR * 2;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  const int kt_all = (int)((a.K + kBK - 1) / kBK);
+  int kts = (kt_all + splits - 1) / splits;
+  kts += kts & 1;                     // slices start on even steps (wide scale / zero loads)
+  splits = (kt_all + kts - 1) / kts;  // every slice gets at least one step
+  const int meta_row = a.mode == W4_MODE_GLOBAL ? 0 : a.mode == W4_MODE_ROWWISE ? 1 : (int)(a.K / a.group);
+  const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
+  const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
+  k<<<grid, 256, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.M, (int)a.N, (int)a.K, meta_row,
+                            log2g, kts, splits > 1 ? part : nullptr);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(part, splits, a.M * a.N, (int)a.N, a.bias, a.Y, st);
+}
+
+template <int FM, int FN, bool KTAIL>
+hipError_t launch_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
+  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL>(a, splits, part, st);
+  const bool g16 = a.group == 16;
+  if (a.K % 128 == 0)
+    return g16 ? launch_cfg<FM, FN, 2, 1, KTAIL>(a, splits, part, st) : launch_cfg<FM, FN, 1, 1, KTAIL>(a, splits, part, st);
+  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL>(a, splits, part, st) : launch_cfg<FM, FN, 1, 2, KTAIL>(a, splits, part, st);
+}
+
+template <int FM, int FN>
+hipError_t launch_tile(const MmArgs& a, int splits, float* part, hipStream_t st) {
+  return a.K % kBK == 0 ? launch_meta<FM, FN, false>(a, splits, part, st) : launch_meta<FM, FN, true>(a, splits, part, st);
+}
+
+}  // namespace
+
+bool gemm_nt_reg_supported(const MmArgs& a) {
+  // 32-bit buffer offsets: a 256-row activation tile must stay below 2 GiB
+  return !a.transposed && a.K <= ((int64_t)1 << 21);
+}
+
+hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st) {
+  return tile == 0 ? launch_tile<4, 1>(a, splits, part, st) : launch_tile<8, 1>(a, splits, part, st);
+}
+
+}  // namespace w4

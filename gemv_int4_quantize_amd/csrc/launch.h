@@ -51,4 +51,13 @@ size_t gemm_lds_bytes(const MmArgs& a);
 size_t gemm_workspace_bytes(const MmArgs& a);
 hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 
+// Non-transposed GEMM with the weight operand dequantized into MFMA registers
+// (tile 0: 128 x 128, tile 1: 256 x 128); split-K over `part` when splits > 1.
+bool gemm_nt_reg_supported(const MmArgs& a);
+hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st);
+
+// Y = sum of `splits` fp32 planes of `total` values (fixed order) + bias[i % outc].
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t total, int outc, const float* bias, float* Y,
+                                hipStream_t st);
+
 }  // namespace w4
