@@ -146,7 +146,7 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
       static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
       const w4::MmArgs a = make_args(dummy, M, reinterpret_cast<const int32_t*>(dummy), dummy, dummy, desc,
                                      op == W4_OP_MM_T, nullptr, nullptr);
-      if (!w4::gemv_supported(a, device_caps())) *bytes = w4::gemm_workspace_bytes(a);
+      if (!w4::gemv_supported(a, device_caps())) *bytes = w4::gemm_workspace_bytes(a, device_caps());
       break;
     }
     default: return fail(W4_ERR_INVALID, "op = %d is unknown", op);
@@ -200,11 +200,11 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   const w4::MmArgs a = make_args(A, M, packed, scales, zeros, desc, transposed, bias, Y);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (w4::gemv_supported(a, device_caps())) return launched(w4::launch_gemv(a, device_caps(), st), "gemv");
-  if (w4::gemm_lds_bytes(a) > device_lds_limit())
-    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a),
+  if (w4::gemm_lds_bytes(a, device_caps()) > device_lds_limit())
+    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a, device_caps()),
                 device_lds_limit());
   if (ws != nullptr && !aligned(ws, 16)) return fail(W4_ERR_ALIGN, "workspace must be 16-byte aligned");
-  return launched(w4::launch_gemm(a, ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
+  return launched(w4::launch_gemm(a, device_caps(), ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
 }
 
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
@@ -217,7 +217,7 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, nullptr,
                                  nullptr);
   if (w4::gemv_supported(a, device_caps())) return w4::gemv_name(a);
-  return w4::gemm_name(a, true);
+  return w4::gemm_name(a, device_caps(), true);
 }
 
 const char* w4_status_string(int status) {

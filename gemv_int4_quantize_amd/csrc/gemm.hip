@@ -27,6 +27,7 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 
@@ -63,6 +64,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* As = smem;                          // [STAGES][BM][LR]
   uint16_t* Bs = smem + STAGES * BM * LR;       // [STAGES][BN][LR]
+  // Transposed mode: the weight tile is written column-wise (rows 8 apart per lane), which
+  // puts the lanes of one LDS write in the same banks; XOR-ing the 16-byte chunk index of
+  // row k with (k / 16) spreads them while the 16 consecutive rows of an MFMA operand read
+  // keep one swizzle value (so reads stay conflict-free).  Element offset e of row k.
+  auto bswz = [](int k, int e) -> int {
+    if constexpr (!TRANS) return e;
+    else return ((((e >> 3) ^ (k >> 4)) & (BK / 8 - 1)) << 3) | (e & 7);
+  };
 
   const int L = TRANS ? N : K;      // contraction length
   const int OUTC = TRANS ? K : N;   // output columns
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       for (int i = 0; i < W_PER_T; ++i) dq_word_f32(R.w[i], dq_const_mix(R.s[i], R.z[i]), v[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint16_t* dst = bs + (wc * 8 + j) * LR + rb * W_PER_T;
+        uint16_t* dst = bs + (wc * 8 + j) * LR + bswz(wc * 8 + j, rb * W_PER_T);
         if constexpr (W_PER_T == 8) {
           *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
                                                  pack_bf16x2(v[4][j], v[5][j]), pack_bf16x2(v[6][j], v[7][j])};
@@ -207,14 +216,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   const int lk = (lane >> 5) * 8;
   auto compute = [&](int buf) {
     const uint16_t* as = As + buf * BM * LR + (wm * FM * 32 + lr) * LR + lk;
-    const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR + lk;
+    const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LR + kk * 16);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + kk * 16);
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -321,22 +331,24 @@ namespace {
 // Tile configurations.  kind 0: the LDS-staged kernel above (both directions; the
 // non-transposed form only serves contractions too long for the register-operand kernel);
 // kind 1 / 2: the non-transposed register-operand kernel (gemm_nt.hip) with 128 x 128 /
-// 256 x 128 tiles.  `eff`: throughput of a full tile relative to the best of its
-// direction, measured on MI355X at the fine-tune shapes.
+// 256 x 128 tiles.  slots: workgroups resident per CU; full: workgroups per CU needed for
+// full throughput; eff: throughput of a full tile relative to the best of its direction,
+// all measured on MI355X at the fine-tune shapes.
 struct Cfg {
   int kind;
   int wm, wn, fm, fn, bk, stages;
   const char* name;
   bool transposed;
+  int slots, full;
   float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {0, 2, 2, 4, 4, 64, 2, "gemm_t_256x256", true, 1.0f},
-    {0, 4, 2, 2, 2, 64, 2, "gemm_t_256x128", true, 0.82f},
-    {0, 2, 2, 2, 2, 32, 3, "gemm_t_128x128", true, 0.64f},
-    {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 1.0f},
-    {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 0.96f},
-    {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 0.7f},
+    {0, 2, 2, 4, 4, 64, 2, "gemm_t_256x256", true, 1, 1, 1.0f},
+    {0, 4, 2, 2, 2, 64, 2, "gemm_t_256x128", true, 1, 1, 0.98f},
+    {0, 2, 2, 2, 2, 32, 3, "gemm_t_128x128", true, 2, 2, 0.8f},
+    {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 1.0f},
+    {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 2, 2, 1.0f},
+    {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 1, 1, 0.7f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
@@ -346,10 +358,11 @@ struct Plan {
   int splits;
 };
 
-// Choose the tile configuration and the split-K factor.  score = full-tile efficiency x
-// how well the workgroups fill the CUs in whole waves x how much of the edge tiles is
-// real work / (1 + the cost of writing and re-reading the split-K partial sums).
-Plan pick_plan(const MmArgs& a, bool allow_split) {
+// Choose the tile configuration and the split-K factor: score = full-tile efficiency x
+// utilisation x edge-tile useful fraction / (1 + cost of the split-K partial planes).
+// Utilisation: with all workgroups resident at once, min(1, workgroups / (CUs x full));
+// over several rounds, the filled fraction of the rounds.
+Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
   static const int forced = [] {
     // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
     const char* e = getenv("W4A16_GEMM_CFG");
@@ -358,27 +371,32 @@ Plan pick_plan(const MmArgs& a, bool allow_split) {
   const int64_t outc = a.transposed ? a.K : a.N;
   const int64_t L = a.transposed ? a.N : a.K;
   const bool reg_ok = gemm_nt_reg_supported(a);
-  Plan best{a.transposed ? 2 : (reg_ok ? 3 : kNtLdsCfg), 1};
+  const int64_t cus = caps.cus > 0 ? caps.cus : 256;
+  Plan best{a.transposed ? 1 : (reg_ok ? 3 : kNtLdsCfg), 1};
   float best_score = -1.0f;
   for (int i = 0; i < kNumCfgs; ++i) {
     const Cfg& c = kCfgs[i];
     if (c.transposed != a.transposed) continue;
     if (!a.transposed && (c.kind != 0) != reg_ok) continue;
     if (forced >= 0 && forced < kNumCfgs && kCfgs[forced].transposed == a.transposed && i != forced) continue;
-    // waves per workgroup times resident workgroups per CU, in units of one 256-thread group
     const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
     const int64_t tm = (a.M + bm - 1) / bm, tn = (outc + bn - 1) / bn;
     const int64_t kt = (L + c.bk - 1) / c.bk;
-    const int64_t slots = c.kind == 1 ? 3 * 256 : c.kind == 2 ? 2 * 256 : 256;  // resident workgroups
+    const float edge = (float)a.M / (float)(tm * bm) * (float)outc / (float)(tn * bn);
     for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
       if (sp > 1 && kt / sp < 16) break;  // keep >= 16 contraction steps per slice
       const int64_t wgs = tm * tn * sp;
-      const float waves = (float)((wgs + slots - 1) / slots);
-      const float fill = (float)wgs / ((float)slots * waves) * (float)a.M / (float)(tm * bm) *
-                         (float)outc / (float)(tn * bn);
+      const int64_t resident = cus * c.slots;
+      float util;
+      if (wgs <= resident) {
+        util = std::min(1.0f, (float)wgs / (float)(cus * c.full));
+      } else {
+        const int64_t rounds = (wgs + resident - 1) / resident;
+        util = (float)wgs / (float)(rounds * resident);
+      }
       // partial planes: sp writes + sp reads of M x outc fp32 against 2 M outc L flops
       const float over = sp > 1 ? 480.0f * (float)sp / (float)L : 0.0f;
-      const float score = fill * c.eff / (1.0f + over);
+      const float score = c.eff * util * edge / (1.0f + over);
       if (score > best_score) {
         best_score = score;
         best = Plan{i, sp};
@@ -461,22 +479,26 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t total, in
   return hipGetLastError();
 }
 
-const char* gemm_name(const MmArgs& a, bool with_workspace) {
+const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspace) {
   static thread_local char buf[64];
-  const Plan p = pick_plan(a, with_workspace);
+  const Plan p = pick_plan(a, caps, with_workspace);
   const Cfg& c = kCfgs[p.cfg];
   if (p.splits == 1) return c.name;
   snprintf(buf, sizeof(buf), "%s_splitk%d", c.name, p.splits);
   return buf;
 }
 
-size_t gemm_lds_bytes(const MmArgs& a) { return lds_bytes(kCfgs[pick_plan(a, false).cfg]); }
+size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps) {
+  return lds_bytes(kCfgs[pick_plan(a, caps, false).cfg]);
+}
 
-size_t gemm_workspace_bytes(const MmArgs& a) { return split_bytes(a, pick_plan(a, true)); }
+size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps) {
+  return split_bytes(a, pick_plan(a, caps, true));
+}
 
-hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
-  Plan p = pick_plan(a, ws != nullptr);
-  if (p.splits > 1 && split_bytes(a, p) > ws_bytes) p = pick_plan(a, false);
+hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st) {
+  Plan p = pick_plan(a, caps, ws != nullptr);
+  if (p.splits > 1 && split_bytes(a, p) > ws_bytes) p = pick_plan(a, caps, false);
   return run_plan(a, p, static_cast<float*>(ws), st);
 }
 

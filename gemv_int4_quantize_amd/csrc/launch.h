@@ -46,10 +46,10 @@ hipError_t launch_gemv(const MmArgs& a, const DeviceCaps& caps, hipStream_t st);
 // GEMM: kernel name (with a split-K suffix when a workspace would be used), LDS
 // footprint, the workspace the split-K plan wants (0 if none) and the launch, which
 // splits the contraction only when `ws` holds at least the planned bytes.
-const char* gemm_name(const MmArgs& a, bool with_workspace);
-size_t gemm_lds_bytes(const MmArgs& a);
-size_t gemm_workspace_bytes(const MmArgs& a);
-hipError_t launch_gemm(const MmArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
+const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspace);
+size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps);
+size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps);
+hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st);
 
 // Non-transposed GEMM with the weight operand dequantized into MFMA registers
 // (tile 0: 128 x 128, tile 1: 256 x 128); split-K over `part` when splits > 1.
