@@ -7,6 +7,10 @@
 // the transposed product reads the same packed weights, scales and zeros);
 // "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560).
 //
+// This file holds the LDS-staged kernel, used for the transposed product and, in the
+// non-transposed direction, only for contractions too long for the register-operand
+// kernel of gemm_nt.hip; the tile / split-K planner for both; and the split-K reduction.
+//
 // Structure (one workgroup = WM x WN waves, output tile BM x BN, contraction step BK):
 //   * the activation tile (X or dY, contraction along its rows) goes global -> LDS;
 //   * the packed weight tile is loaded to registers, dequantized in registers with
@@ -14,10 +18,11 @@
 //     rows are output columns and whose BK columns are the contraction, so each MFMA
 //     operand is one 16-byte LDS read in both directions.  Non-transposed, a packed
 //     word already runs along the contraction; transposed, each thread dequantizes a
-//     column of rows of one word and writes it across the contraction axis;
-//   * three LDS stages: the global loads of step k+2 are in flight during the MFMAs of
-//     steps k and k+1, and are dequantized into LDS at the end of step k+1; one
-//     barrier per step;
+//     column of rows of one word and writes it across the contraction axis, into a
+//     tile whose 16-byte chunks are XOR-swizzled by row / 16 (conflict-free writes and
+//     operand reads);
+//   * two or three LDS stages: the global loads of step k+1 (k+2) are in flight during
+//     the MFMAs of step k; one barrier per step;
 //   * LDS rows are padded by 16 bytes so the rows read by one MFMA operand load fall
 //     in distinct banks;
 //   * v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains twice the rate of the
