@@ -354,6 +354,11 @@ constexpr Cfg kCfgs[] = {
     {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 1.0f},
     {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 2, 2, 1.0f},
     {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 1, 1, 0.7f},
+    // short-M tiles (5 <= M < 128): fewer rows per tile waste less of it; the dequantization
+    // is then shared by fewer rows, so their full-tile efficiency is lower
+    {3, 1, 4, 2, 1, 64, 2, "gemm_nt_64x128", false, 4, 2, 0.85f},
+    {4, 1, 4, 1, 1, 64, 2, "gemm_nt_32x128", false, 4, 2, 0.5f},
+    {0, 1, 4, 1, 1, 64, 2, "gemm_t_32x128", true, 3, 2, 0.3f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
@@ -419,7 +424,7 @@ size_t split_bytes(const MmArgs& a, const Plan& p) {
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
 
 size_t lds_bytes(const Cfg& c) {
-  if (c.kind != 0) return (size_t)2 * c.fm * 32 * (c.bk + 8) * 2;  // two activation buffers
+  if (c.kind != 0) return (size_t)2 * c.wm * c.fm * 32 * (c.bk + 8) * 2;  // two activation buffers
   return (size_t)c.stages * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
 }
 
@@ -465,12 +470,15 @@ hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st)
     switch (p.cfg) {
       case 0: return run_meta<true, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
       case 1: return run_meta<true, 4, 2, 2, 2, 64, 2>(a, p.splits, part, st);
+      case 8: return run_meta<true, 1, 4, 1, 1, 64, 2>(a, p.splits, part, st);
       default: return run_meta<true, 2, 2, 2, 2, 32, 3>(a, p.splits, part, st);
     }
   }
   switch (kCfgs[p.cfg].kind) {
     case 1: return launch_gemm_nt_reg(a, 0, p.splits, part, st);
     case 2: return launch_gemm_nt_reg(a, 1, p.splits, part, st);
+    case 3: return launch_gemm_nt_reg(a, 2, p.splits, part, st);
+    case 4: return launch_gemm_nt_reg(a, 3, p.splits, part, st);
     default: return run_meta<false, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
   }
 }

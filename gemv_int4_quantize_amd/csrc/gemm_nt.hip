@@ -336,7 +336,12 @@ bool gemm_nt_reg_supported(const MmArgs& a) {
 }
 
 hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st) {
-  return tile == 0 ? launch_tile<4, 1>(a, splits, part, st) : launch_tile<8, 1>(a, splits, part, st);
+  switch (tile) {
+    case 0: return launch_tile<4, 1>(a, splits, part, st);  // 128 x 128
+    case 1: return launch_tile<8, 1>(a, splits, part, st);  // 256 x 128
+    case 2: return launch_tile<2, 1>(a, splits, part, st);  // 64 x 128
+    default: return launch_tile<1, 1>(a, splits, part, st);  // 32 x 128
+  }
 }
 
 }  // namespace w4

@@ -52,7 +52,8 @@ size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps);
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st);
 
 // Non-transposed GEMM with the weight operand dequantized into MFMA registers
-// (tile 0: 128 x 128, tile 1: 256 x 128); split-K over `part` when splits > 1.
+// (tile 0: 128 x 128, 1: 256 x 128, 2: 64 x 128, 3: 32 x 128); split-K over `part`
+// when splits > 1.
 bool gemm_nt_reg_supported(const MmArgs& a);
 hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st);
 

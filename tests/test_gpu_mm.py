@@ -146,6 +146,25 @@ def test_fused_qkv_equivalence():
             assert_mm_close(dxf, dxs, f"fused T {mode} M={M}")
 
 
+SHORT_M_CASES = [(8, 4096, 2048, False, "gemm_nt_32x128"), (40, 4096, 2048, False, "gemm_nt_32x128"),
+                 (96, 8192, 4096, False, "gemm_nt_64x128"), (24, 8192, 2048, True, "gemm_t_32x128"),
+                 (64, 12288, 4096, True, "gemm_t_32x128")]
+
+
+@pytest.mark.parametrize("ci", range(len(SHORT_M_CASES)),
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}{'t' if c[3] else 'nt'}" for c in SHORT_M_CASES])
+def test_short_m_tiles(ci):
+    """5 <= M < 128 runs the 32- and 64-row tiles (with split-K); parity with the oracle."""
+    M, N, K, t, name = SHORT_M_CASES[ci]
+    print(f"[case] short M={M} N={N} K={K} t={t}", flush=True)
+    assert w4.kernel_for(M, N, K, "groupwise", 128, transposed=t).startswith(name)
+    _, ref, qw = _setup(708, ci, N, K, "groupwise", 128)
+    a = synth.activations_bf16(708, ci, M, N if t else K)
+    bias = synth.bias_f32(708, ci, K if t else N)
+    y = w4.mm(dev_bf16(a), qw, transposed=t, bias=dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(a, *ref, K, t, bias), f"short M {ci}")
+
+
 SPLITK_CASES = [(64, 4104, 4096, True, "groupwise", 128), (64, 4096, 4128, False, "groupwise", 32),
                 (160, 4096, 4096, False, "rowwise", None), (300, 2056, 4096, True, "groupwise", 64),
                 (96, 8200, 2048, True, "global", None), (33, 3000, 8192, False, "groupwise", 256)]
