@@ -171,6 +171,7 @@ def bench_gemm(torch, w4, synth, reps: int):
     import numpy as np
     log("QLoRA GEMM pair: 3 shapes x {rowwise, g64} x M in {1024, 2048, 4096} x {NT, T}")
     pts = []
+    layer = []
     for si, (N, K) in enumerate(QLORA_SHAPES):
         if si == 0:
             parts = [dev_bf16(torch, synth.weight(4, 0, 4096, K, "bf16", tensor_id=synth.T_Q + i)) for i in range(3)]
@@ -194,6 +195,23 @@ def bench_gemm(torch, w4, synth, reps: int):
                             "t_us": round(t_t * 1e6, 1),
                             "nt_kernel": w4.kernel_for(M, N, K, mode, g), "t_kernel": w4.kernel_for(M, N, K, mode, g,
                                                                                                    True)})
+                if g is None:
+                    # the QLoRA layer step (forward + backward dX) against the reference path of the
+                    # page: dequantize the frozen weight to bf16 every step, then two bf16 matmuls
+                    # (torch / hipBLASLt); also the two bf16 matmuls alone, as if W were stored in bf16
+                    F = torch.nn.functional
+                    wd16 = w4.dequantize(qw, torch.bfloat16)
+                    fused = [lambda: w4.mm(x, qw, out=y), lambda: w4.mm(dy, qw, transposed=True, out=dx)]
+                    ref = [lambda: w4.dequantize(qw, torch.bfloat16), lambda: F.linear(x, wd16),
+                           lambda: torch.mm(dy, wd16)]
+                    dense = [lambda: F.linear(x, wd16), lambda: torch.mm(dy, wd16)]
+                    run_batch(torch, ref + dense)
+                    t_f = run_batch(torch, fused * reps) / reps * 1e-3
+                    t_r = run_batch(torch, ref * reps) / reps * 1e-3
+                    t_d = run_batch(torch, dense * reps) / reps * 1e-3
+                    layer.append({"M": M, "N": N, "K": K, "fused_us": round(t_f * 1e6, 1),
+                                  "dequant_ref_us": round(t_r * 1e6, 1), "dense_bf16_us": round(t_d * 1e6, 1)})
+                    del wd16
                 del x, dy, y, dx
             del qw
         torch.cuda.empty_cache()
@@ -209,7 +227,16 @@ def bench_gemm(torch, w4, synth, reps: int):
         "t_over_nt_total": round(t_t / t_nt, 3),
         "t_over_nt_max": max(p["t_over_nt"] for p in pts),
         "min_tflops_m_ge_512": min(min(p["nt_tflops"], p["t_tflops"]) for p in big),
+        "qlora_layer_step": {
+            "workload": "forward + backward dX of a frozen rowwise int4 layer at the same shapes and M",
+            "fused_ms": round(sum(p["fused_us"] for p in layer) * 1e-3, 3),
+            "dequant_ref_ms": round(sum(p["dequant_ref_us"] for p in layer) * 1e-3, 3),
+            "dense_bf16_ms": round(sum(p["dense_bf16_us"] for p in layer) * 1e-3, 3),
+            "speedup_vs_dequant_ref": round(sum(p["dequant_ref_us"] for p in layer) /
+                                            sum(p["fused_us"] for p in layer), 3),
+        },
         "points": pts,
+        "layer_points": layer,
     }
 
 
@@ -359,11 +386,12 @@ def main() -> int:
     details = {"gemv": g["points"]}
     if not args.no_extras:
         gm = bench_gemm(torch, w4, synth, reps=5)
-        result["gemm"] = {k: v for k, v in gm.items() if k != "points"}
+        result["gemm"] = {k: v for k, v in gm.items() if k not in ("points", "layer_points")}
         result["gemm"]["roofline"] = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                       "achieved_nt": gm["nt_tflops"], "achieved_t": gm["t_tflops"],
                                       "frac_nt": gm["nt_frac_of_peak"], "frac_t": gm["t_frac_of_peak"]}
         details["gemm"] = gm["points"]
+        details["qlora_layer"] = gm["layer_points"]
         log(f"GEMM: NT {gm['nt_tflops']} TFLOP/s, T {gm['t_tflops']} TFLOP/s, T/NT {gm['t_over_nt_total']}")
         qz = bench_quantize(torch, w4, synth, reps=5)
         result["quantize"] = {"workload": qz["workload"],

@@ -17,5 +17,6 @@ from .ops import (  # noqa: F401
     quantize_pack,
     quantize_pack_into,
 )
+from .layer import W4A16Linear, w4a16_linear  # noqa: F401
 
 __version__ = "0.1.0"

@@ -1,0 +1,76 @@
+"""Frozen int4 linear layer with autograd, for QLoRA-style fine-tuning.
+
+Forward ``Y = X @ w^T (+ bias)`` runs the W4A16 GEMV / GEMM; backward
+``dX = dY @ w`` runs the transposed GEMM on the same packed buffer, with no
+repacking and no reshaping of scales or zeros.  The base weight is frozen: no
+gradient is produced for it (nor for the base bias).  Source: "Re-write HQQ Fused
+Gemm Transpose" (pytorch/ao #185), which fine-tunes a frozen 4-bit base with LoRA
+adapters and needs exactly these two products of one packed weight.
+
+The library's matmul accumulates and returns fp32; activations and incoming
+gradients enter it as bf16 (a dtype conversion here is argument marshalling, the
+products themselves run in the gfx950 kernels).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import ops
+from .ops import QuantizedWeight
+
+
+class _W4A16Matmul(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, qw: QuantizedWeight, bias: torch.Tensor | None):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1])
+        if x2.dtype != torch.bfloat16:
+            x2 = x2.to(torch.bfloat16)
+        y = ops.mm(x2.contiguous(), qw, bias=bias)
+        ctx.qw = qw
+        ctx.x_dtype = x.dtype
+        ctx.lead = lead
+        return y.view(*lead, qw.N)
+
+    @staticmethod
+    def backward(ctx, gy: torch.Tensor):
+        qw: QuantizedWeight = ctx.qw
+        g2 = gy.reshape(-1, qw.N)
+        if g2.dtype != torch.bfloat16:
+            g2 = g2.to(torch.bfloat16)
+        dx = ops.mm(g2.contiguous(), qw, transposed=True)
+        return dx.view(*ctx.lead, qw.K).to(ctx.x_dtype), None, None
+
+
+def w4a16_linear(x: torch.Tensor, qw: QuantizedWeight, bias: torch.Tensor | None = None) -> torch.Tensor:
+    """Differentiable ``x @ w^T (+ bias)`` over a packed int4 weight (fp32 result)."""
+    return _W4A16Matmul.apply(x, qw, bias)
+
+
+class W4A16Linear(torch.nn.Module):
+    """A frozen int4 base linear layer: ``forward(x) = x @ w^T (+ bias)``, fp32 output."""
+
+    def __init__(self, qw: QuantizedWeight, bias: torch.Tensor | None = None):
+        super().__init__()
+        self.qw = qw
+        if bias is not None:
+            bias = bias.detach().to(torch.float32).contiguous()
+        self.register_buffer("bias", bias)
+
+    @classmethod
+    def from_weight(cls, weight: torch.Tensor, mode: str = "rowwise", group: int | None = None,
+                    bias: torch.Tensor | None = None) -> "W4A16Linear":
+        """Quantize a [N][K] fp32 / fp16 / bf16 device weight and wrap it."""
+        return cls(ops.quantize_pack(weight, mode, group), bias)
+
+    @property
+    def in_features(self) -> int:
+        return self.qw.K
+
+    @property
+    def out_features(self) -> int:
+        return self.qw.N
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return w4a16_linear(x, self.qw, self.bias)
