@@ -49,7 +49,9 @@ constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
 // META: 0 one (scale, zero) per row (rowwise / global), 1 groupwise with one wide load per
 // two steps, 2 groupwise with one pair per step.  GPW: groups per 32-value lane chunk
 // (2 when g = 16).  KTAIL: K % 64 != 0 (activation columns past K are zeroed in LDS).
-template <int FM, int FN, int GPW, int META, bool KTAIL>
+// WB (META 1): bytes of one wide load = 2 max(1, 128 / g), a compile-time width so that the
+// loop holds exactly one load form.
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB>
 __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -95,8 +97,6 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
     for (int q = 0; q < GPW; ++q) m_off[j][q] = mrow_off[j] + (((uint32_t)(h * 32 + q * 16) >> log2g) * 2);
   }
-  // META 1: bytes of one wide load = 2 * max(1, 128 / g)
-  const int wide_bytes = (128 >> log2g) >= 1 ? (128 >> log2g) * 2 : 2;
 
   struct ARegs {
     u32x4 a[AU];
@@ -135,15 +135,15 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const uint32_t o = mrow_off[j] + mk;
-      if (wide_bytes == 16) {
+      if constexpr (WB == 16) {
         R.s[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
         R.z[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, o, 0, 0));
-      } else if (wide_bytes == 8) {
+      } else if constexpr (WB == 8) {
         const u32x2v a = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(sr, o, 0, 0));
         const u32x2v b = __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(zr, o, 0, 0));
         R.s[j] = u32x4{a[0], a[1], 0u, 0u};
         R.z[j] = u32x4{b[0], b[1], 0u, 0u};
-      } else if (wide_bytes == 4) {
+      } else if constexpr (WB == 4) {
         R.s[j] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(sr, o, 0, 0), 0u, 0u, 0u};
         R.z[j] = u32x4{__builtin_amdgcn_raw_buffer_load_b32(zr, o, 0, 0), 0u, 0u, 0u};
       } else {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < GPW; ++q) {
-        const int e = GPW == 2 ? 4 * p + 2 * h + q : wide_bytes == 8 ? 2 * p + h : wide_bytes == 4 ? p : 0;
+        const int e = GPW == 2 ? 4 * p + 2 * h + q : WB == 8 ? 2 * p + h : WB == 4 ? p : 0;
         dc[j][q] = dq_const_mix(half_of(R.s[j], e), half_of(R.z[j], e));
       }
   };
@@ -291,9 +291,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 }
 
-template <int FM, int FN, int GPW, int META, bool KTAIL>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB = 0>
 hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL>;
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB>;
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   const int lds = 2 * BM * kLR * 2;
   if (lds > 64 * 1024) {
@@ -318,8 +318,14 @@ template <int FM, int FN, bool KTAIL>
 hipError_t launch_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
   if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL>(a, splits, part, st);
   const bool g16 = a.group == 16;
-  if (a.K % 128 == 0)
-    return g16 ? launch_cfg<FM, FN, 2, 1, KTAIL>(a, splits, part, st) : launch_cfg<FM, FN, 1, 1, KTAIL>(a, splits, part, st);
+  if (a.K % 128 == 0) {
+    switch (a.group) {
+      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16>(a, splits, part, st);
+      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8>(a, splits, part, st);
+      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4>(a, splits, part, st);
+      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2>(a, splits, part, st);
+    }
+  }
   return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL>(a, splits, part, st) : launch_cfg<FM, FN, 1, 2, KTAIL>(a, splits, part, st);
 }
 
