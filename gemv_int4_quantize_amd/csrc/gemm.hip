@@ -22,7 +22,10 @@
 //     tile whose 16-byte chunks are XOR-swizzled by row / 16 (conflict-free writes and
 //     operand reads);
 //   * two or three LDS stages: the global loads of step k+1 (k+2) are in flight during
-//     the MFMAs of step k; one barrier per step;
+//     the MFMAs of step k; one barrier per step.  The transposed tiles use the interleaved
+//     form (STAGES = 4): two LDS stages, loads two steps ahead, and the dequantization and
+//     LDS writes of step k+1 cut into slices issued between the MFMAs of step k (with one
+//     wave per SIMD at the 256 x 256 tile, nothing else would overlap that work);
 //   * LDS rows are padded by 16 bytes so the rows read by one MFMA operand load fall
 //     in distinct banks;
 //   * v_mfma_f32_32x32x16_bf16 (on gfx950 it sustains twice the rate of the
@@ -47,7 +50,8 @@ constexpr int lds_row() { return BK + 8; }
 
 // MPT: scale / zero pairs a thread loads per stage in the non-transposed mode: 1 when
 // one group covers all of its words (rowwise, global, or g >= its span), else one per word.
-// STAGES: 2 (loads of step k+1 in flight during step k) or 3 (loads of step k+2).
+// STAGES: 2 (loads of step k+1 in flight during step k), 3 (loads of step k+2), or 4 (two LDS
+// stages, loads of step k+2, stores of step k+1 interleaved with the MFMAs of step k).
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A,
                                                             const int32_t* __restrict__ packed,
@@ -66,9 +70,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   constexpr int W_PER_T = BN * SLOTS / T;       // packed words per thread per stage
   static_assert(W_PER_T >= 1 && W_PER_T <= 8 && BN * SLOTS % T == 0, "weight tile split");
 
+  constexpr int LST = STAGES == 4 ? 2 : STAGES;  // LDS stages (4: two, interleaved stores)
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* As = smem;                          // [STAGES][BM][LR]
-  uint16_t* Bs = smem + STAGES * BM * LR;       // [STAGES][BN][LR]
+  uint16_t* As = smem;                          // [LST][BM][LR]
+  uint16_t* Bs = smem + LST * BM * LR;          // [LST][BN][LR]
   // Transposed mode: the weight tile is written column-wise (rows 8 apart per lane), which
   // puts the lanes of one LDS write in the same banks; XOR-ing the 16-byte chunk index of
   // row k with (k / 16) spreads them while the 16 consecutive rows of an MFMA operand read
@@ -238,7 +243,91 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     }
   };
 
-  if constexpr (STAGES == 2) {
+  // STAGES == 4 (transposed only): the MFMAs of one step read LDS buffer `buf` while the
+  // next step's staged registers R are dequantized and written to buffer `sbuf`, the work
+  // cut into one slice per 16-wide sub-step so that it issues between the MFMAs: activation
+  // units, then weight words dequantized two rows at a time and rounded to bf16 pairs; the
+  // transposed 16-byte rows are written once all W_PER_T rows of a word column are packed.
+  auto compute_store = [&](int buf, const Regs& R, int kt_s, int sbuf) {
+    static_assert(STAGES != 4 || (TRANS && W_PER_T >= 2 && W_PER_T % 2 == 0), "interleaved stores: transposed tiles");
+    if constexpr (STAGES == 4) {
+    constexpr int KK = BK / 16;
+    constexpr int AU_PER = (A_UNITS + KK - 1) / KK;
+    const uint16_t* as = As + buf * BM * LR + (wm * FM * 32 + lr) * LR + lk;
+    const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR;
+    uint16_t* asw = As + sbuf * BM * LR;
+    uint16_t* bsw = Bs + sbuf * BN * LR;
+    constexpr int WCOLS = BN / 8;
+    const int wc = tid % WCOLS;
+    const int rb = tid / WCOLS;
+    uint32_t pk[W_PER_T / 2][8];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LR + kk * 16);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      // slice kk of the next step's stores
+#pragma unroll
+      for (int q = 0; q < AU_PER; ++q) {
+        const int i = kk * AU_PER + q;
+        if (i < A_UNITS) {
+          const int u = tid + i * T;
+          const int row = u / SLOTS, slot = u % SLOTS;
+          const bool in = (KB + kt_s) * BK + slot * 8 < L;
+          *reinterpret_cast<u32x4*>(asw + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int pp = 0; pp < W_PER_T / 2; ++pp) {
+        const int i = 2 * pp;  // rows i, i + 1 of the word column, in slice pp * KK / pairs
+        if (pp * KK / (W_PER_T / 2) == kk) {
+          float v0[8], v1[8];
+          dq_word_f32(R.w[i], dq_const_mix(R.s[i], R.z[i]), v0);
+          dq_word_f32(R.w[i + 1], dq_const_mix(R.s[i + 1], R.z[i + 1]), v1);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pk[i / 2][j] = pack_bf16x2(v0[j], v1[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint16_t* dst = bsw + (wc * 8 + j) * LR + bswz(wc * 8 + j, rb * W_PER_T);
+      if constexpr (W_PER_T == 8) *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0][j], pk[1][j], pk[2][j], pk[3][j]};
+      else if constexpr (W_PER_T == 4) *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0][j], pk[1][j]};
+      else *reinterpret_cast<uint32_t*>(dst) = pk[0][j];
+    }
+    }
+  };
+
+  if constexpr (STAGES == 4) {
+    // Two LDS stages and two register stages: the loads of step k + 2 are issued before
+    // the MFMAs of step k, and step k + 1 (staged during step k - 1) is dequantized and
+    // stored in slices between the MFMAs of step k.  Loads past the contraction read
+    // clamped (valid) addresses; what they stage is never computed.
+    Regs R0, R1;
+    load_stage(0, R0);
+    load_stage(min(1, KT - 1), R1);
+    store_stage(0, R0, 0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      load_stage(kt + 2, R0);
+      compute_store(0, R1, kt + 1, 1);
+      __syncthreads();
+      load_stage(kt + 3, R1);
+      compute_store(1, R0, kt + 2, 0);
+      __syncthreads();
+    }
+    if (kt < KT) compute(0);
+  } else if constexpr (STAGES == 2) {
     // Two LDS stages, one register stage: the loads of step k+1 are issued before the
     // MFMAs of step k and dequantized into the other LDS buffer after them.
     Regs R0;
@@ -348,9 +437,9 @@ struct Cfg {
   float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {0, 2, 2, 4, 4, 64, 2, "gemm_t_256x256", true, 1, 1, 1.0f},
-    {0, 4, 2, 2, 2, 64, 2, "gemm_t_256x128", true, 1, 1, 0.98f},
-    {0, 2, 2, 2, 2, 32, 3, "gemm_t_128x128", true, 2, 2, 0.8f},
+    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 1.0f},
+    {0, 4, 2, 2, 2, 64, 4, "gemm_t_256x128", true, 1, 1, 0.95f},
+    {0, 2, 2, 2, 2, 32, 4, "gemm_t_128x128", true, 3, 2, 0.65f},
     {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 1.0f},
     {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 2, 2, 1.0f},
     {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 1, 1, 0.7f},
@@ -358,7 +447,7 @@ constexpr Cfg kCfgs[] = {
     // is then shared by fewer rows, so their full-tile efficiency is lower
     {3, 1, 4, 2, 1, 64, 2, "gemm_nt_64x128", false, 4, 2, 0.85f},
     {4, 1, 4, 1, 1, 64, 2, "gemm_nt_32x128", false, 4, 2, 0.5f},
-    {0, 1, 4, 1, 1, 64, 2, "gemm_t_32x128", true, 3, 2, 0.3f},
+    {0, 1, 4, 1, 1, 64, 4, "gemm_t_32x128", true, 3, 2, 0.3f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
@@ -425,7 +514,7 @@ int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == 
 
 size_t lds_bytes(const Cfg& c) {
   if (c.kind != 0) return (size_t)2 * c.wm * c.fm * 32 * (c.bk + 8) * 2;  // two activation buffers
-  return (size_t)c.stages * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
+  return (size_t)(c.stages == 4 ? 2 : c.stages) * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
@@ -436,7 +525,7 @@ hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
   const bool one = TRANS || META != META_GROUP || a.group >= 8 * WPT;
   auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES>
                : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES>;
-  const size_t lds = (size_t)STAGES * (BM + BN) * (BK + 8) * 2;
+  const size_t lds = (size_t)(STAGES == 4 ? 2 : STAGES) * (BM + BN) * (BK + 8) * 2;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
@@ -468,10 +557,10 @@ hipError_t run_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
 hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st) {
   if (a.transposed) {
     switch (p.cfg) {
-      case 0: return run_meta<true, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
-      case 1: return run_meta<true, 4, 2, 2, 2, 64, 2>(a, p.splits, part, st);
-      case 8: return run_meta<true, 1, 4, 1, 1, 64, 2>(a, p.splits, part, st);
-      default: return run_meta<true, 2, 2, 2, 2, 32, 3>(a, p.splits, part, st);
+      case 0: return run_meta<true, 2, 2, 4, 4, 64, 4>(a, p.splits, part, st);
+      case 1: return run_meta<true, 4, 2, 2, 2, 64, 4>(a, p.splits, part, st);
+      case 8: return run_meta<true, 1, 4, 1, 1, 64, 4>(a, p.splits, part, st);
+      default: return run_meta<true, 2, 2, 2, 2, 32, 4>(a, p.splits, part, st);
     }
   }
   switch (kCfgs[p.cfg].kind) {
