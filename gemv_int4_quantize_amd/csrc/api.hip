@@ -96,6 +96,11 @@ int check_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   if (desc->K % 32 != 0) return fail(W4_ERR_UNSUPPORTED, "matmul needs K %% 32 == 0 (K = %lld)", (long long)desc->K);
   if (transposed && desc->N % 8 != 0)
     return fail(W4_ERR_UNSUPPORTED, "transposed matmul needs N %% 8 == 0 (N = %lld)", (long long)desc->N);
+  // the transposed GEMM addresses a 256-row activation tile and 64 weight rows per step
+  // with 32-bit buffer offsets
+  if (transposed && (desc->N >= ((int64_t)1 << 22) || desc->K > ((int64_t)1 << 21)))
+    return fail(W4_ERR_UNSUPPORTED, "transposed matmul needs N < 2^22 and K <= 2^21 (N = %lld, K = %lld)",
+                (long long)desc->N, (long long)desc->K);
   if (!aligned(A, 16) || !aligned(packed, 16)) return fail(W4_ERR_ALIGN, "A and packed must be 16-byte aligned");
   if (!aligned(Y, 4) || (bias && !aligned(bias, 4)) || !aligned(scales, 2) || !aligned(zeros, 2))
     return fail(W4_ERR_ALIGN, "Y / bias must be 4-byte and scales / zeros 2-byte aligned");

@@ -42,6 +42,12 @@
 namespace w4 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// raw buffer resource (gfx9-class dword 3: 32-bit data format); loads past `bytes` read 0
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 
 // LDS rows hold BK contraction values plus 8 bf16 of padding: a row stride of
 // (BK + 8) * 2 bytes puts the 16-byte operand reads of consecutive rows in distinct banks.
@@ -111,8 +117,95 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     else return (size_t)n * gpr + ((wcol * 8) >> log2g);
   };
 
+  // Transposed mode: buffer loads at per-thread offsets fixed for the whole contraction,
+  // so a step adds one scalar to them.  Activations: one resource over the tile's rows
+  // (rows past M read as zero).  Weights and scale / zero: a resource over the step's BK
+  // contraction rows, rebuilt per step from scalars (rows past N read as zero: code 0,
+  // scale 0, zero 0 dequantize to 0, against zeroed activation columns).
+  constexpr int WCOLS = BN / 8;
+  rsrc_t t_ar = make_rsrc(A, 0);
+  uint32_t t_aoff[A_UNITS] = {};
+  uint32_t t_woff = 0, t_moff = 0;
+  uint16_t t_gs = 0, t_gz = 0;
+  if constexpr (TRANS) {
+    // N < 2^22 and K <= 2^21 (checked at the boundary) keep every offset below 2^32
+    t_ar = make_rsrc(A + (size_t)m0 * L, (uint32_t)__builtin_amdgcn_readfirstlane(min(BM, M - m0)) * (uint32_t)L * 2u);
+#pragma unroll
+    for (int i = 0; i < A_UNITS; ++i) {
+      const int u = tid + i * T;
+      t_aoff[i] = ((uint32_t)(u / SLOTS) * (uint32_t)L + (uint32_t)(u % SLOTS) * 8u) * 2u;
+    }
+    const int wc = tid % WCOLS, rb = tid / WCOLS;
+    const int wcol = min((c0 >> 3) + wc, KW - 1);
+    t_woff = ((uint32_t)(rb * W_PER_T) * (uint32_t)KW + (uint32_t)wcol) * 4u;
+    // groupwise: row rb * W_PER_T's pair of the word column's group; rowwise: that row's pair
+    if constexpr (META == META_GROUP)
+      t_moff = ((uint32_t)(rb * W_PER_T) * (uint32_t)gpr + (uint32_t)((wcol * 8) >> log2g)) * 2u;
+    else
+      t_moff = (uint32_t)(rb * W_PER_T) * 2u;
+    if constexpr (META == META_GLOBAL) {
+      t_gs = scales[0];
+      t_gz = zeros[0];
+    }
+  }
+
   auto load_stage = [&](int kt, Regs& R) {
     const int l0 = (KB + kt) * BK;
+    if constexpr (TRANS) {
+#pragma unroll
+      for (int i = 0; i < A_UNITS; ++i)
+        R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t_ar, t_aoff[i] + (uint32_t)l0 * 2, 0, 0));
+      // uniform values, kept in scalar registers (a vector min / max here would make the
+      // resource descriptor per-lane and every load a waterfall loop)
+      const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, N - l0)));
+      const int nb = __builtin_amdgcn_readfirstlane(min(l0, N - 1));
+      const rsrc_t pr = make_rsrc(packed + (size_t)nb * KW, (uint32_t)rows * (uint32_t)KW * 4u);
+#pragma unroll
+      for (int i = 0; i < W_PER_T; ++i)
+        R.w[i] = __builtin_amdgcn_raw_buffer_load_b32(pr, t_woff + (uint32_t)(i * KW * 4), 0, 0);
+      if constexpr (META == META_GROUP) {
+        const rsrc_t sr = make_rsrc(scales + (size_t)nb * gpr, (uint32_t)(rows * gpr * 2));
+        const rsrc_t zr = make_rsrc(zeros + (size_t)nb * gpr, (uint32_t)(rows * gpr * 2));
+#pragma unroll
+        for (int i = 0; i < W_PER_T; ++i) {
+          R.s[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, t_moff + (uint32_t)(i * gpr * 2), 0, 0);
+          R.z[i] = __builtin_amdgcn_raw_buffer_load_b16(zr, t_moff + (uint32_t)(i * gpr * 2), 0, 0);
+        }
+      } else if constexpr (META == META_ROW) {
+        // the W_PER_T consecutive rows' pairs in one load per array
+        const rsrc_t sr = make_rsrc(scales + nb, (uint32_t)(rows * 2));
+        const rsrc_t zr = make_rsrc(zeros + nb, (uint32_t)(rows * 2));
+        uint32_t sv[4] = {}, zv[4] = {};
+        if constexpr (W_PER_T == 8) {
+          const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, t_moff, 0, 0));
+          const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, t_moff, 0, 0));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { sv[q] = a[q]; zv[q] = b[q]; }
+        } else if constexpr (W_PER_T == 4) {
+          const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sr, t_moff, 0, 0));
+          const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(zr, t_moff, 0, 0));
+          sv[0] = a[0]; sv[1] = a[1]; zv[0] = b[0]; zv[1] = b[1];
+        } else if constexpr (W_PER_T == 2) {
+          sv[0] = __builtin_amdgcn_raw_buffer_load_b32(sr, t_moff, 0, 0);
+          zv[0] = __builtin_amdgcn_raw_buffer_load_b32(zr, t_moff, 0, 0);
+        } else {
+          sv[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, t_moff, 0, 0);
+          zv[0] = __builtin_amdgcn_raw_buffer_load_b16(zr, t_moff, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < W_PER_T; ++i) {
+          R.s[i] = (uint16_t)(sv[i / 2] >> (16 * (i & 1)));
+          R.z[i] = (uint16_t)(zv[i / 2] >> (16 * (i & 1)));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < W_PER_T; ++i) {
+          R.s[i] = t_gs;
+          R.z[i] = t_gz;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;

@@ -106,7 +106,8 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
  *   transposed != 0: Y[m][k] = sum_n A[m][n] * w[n][k] (+ bias[k]),  A = dY [M][N]
  * where w[n][k] = bf16_rne((q - z) * s).  The transposed mode reads the same
  * packed, scales and zeros buffers.  M == 0 is a no-op.  K % 32 == 0 is
- * required (W4_ERR_UNSUPPORTED otherwise).  A and packed must be 16-byte
+ * required, and the transposed mode also needs N % 8 == 0, N < 2^22 and
+ * K <= 2^21 (W4_ERR_UNSUPPORTED otherwise).  A and packed must be 16-byte
  * aligned, Y and bias 4-byte aligned.  M <= 4 non-transposed runs the
  * memory-bound GEMV (no matrix cores); other shapes run the MFMA GEMM.  ws may
  * always be NULL: the GEMM then runs unsplit.  A workspace of at least the

@@ -103,6 +103,11 @@ def test_mm_validation_before_launch():
     assert _mm(a16, 4, a16, a16, a16, d40) == _lib.W4_ERR_UNSUPPORTED
     dn = _lib.W4Desc(60, 128, _lib.MODE_ROWWISE, 0)
     assert _mm(a16, 4, a16, a16, a16, dn, transposed=1) == _lib.W4_ERR_UNSUPPORTED
+    # transposed: 32-bit buffer offsets bound N and K
+    assert _mm(a16, 4, a16, a16, a16, _lib.W4Desc(1 << 22, 128, _lib.MODE_ROWWISE, 0), transposed=1) == \
+        _lib.W4_ERR_UNSUPPORTED
+    assert _mm(a16, 4, a16, a16, a16, _lib.W4Desc(64, (1 << 21) + 32, _lib.MODE_ROWWISE, 0), transposed=1) == \
+        _lib.W4_ERR_UNSUPPORTED
     # M == 0 is a successful no-op and never touches the pointers
     assert _mm(a16, 0, a16, a16, a16, d) == _lib.W4_OK
 
