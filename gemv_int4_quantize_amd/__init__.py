@@ -12,6 +12,7 @@ from .ops import (  # noqa: F401
     kernel_for,
     meta_shape,
     mm,
+    mm_split,
     mode_id,
     quantize_fused,
     quantize_pack,

@@ -25,12 +25,16 @@ OP_QUANTIZE, OP_MM, OP_MM_T, OP_DEQUANTIZE = 0, 1, 2, 3
 # every entry point declared in include/w4a16.h
 EXPORTS = (
     "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_dequantize", "w4a16_mm",
-    "w4a16_mm_kernel", "w4_status_string", "w4_last_error", "w4_version",
+    "w4a16_mm_out", "w4a16_mm_kernel", "w4_status_string", "w4_last_error", "w4_version",
 )
 
 
 class W4Desc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64), ("mode", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+class W4OutSeg(ctypes.Structure):
+    _fields_ = [("Y", ctypes.c_void_p), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
 
 
 class W4Error(RuntimeError):
@@ -61,6 +65,7 @@ def lib() -> ctypes.CDLL:
     L.w4_quantize_pack.argtypes = [vp, i32, pdesc, vp, vp, vp, vp, sz, vp]
     L.w4_dequantize.argtypes = [vp, vp, vp, pdesc, vp, i32, vp]
     L.w4a16_mm.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp, sz, vp]
+    L.w4a16_mm_out.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz, vp]
     L.w4a16_mm_kernel.argtypes = [i64, pdesc, i32]
     L.w4a16_mm_kernel.restype = ctypes.c_char_p
     L.w4_status_string.argtypes = [i32]
@@ -69,7 +74,8 @@ def lib() -> ctypes.CDLL:
     L.w4_last_error.restype = ctypes.c_char_p
     L.w4_version.argtypes = []
     L.w4_version.restype = ctypes.c_char_p
-    for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_dequantize", "w4a16_mm"):
+    for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_dequantize", "w4a16_mm",
+                 "w4a16_mm_out"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -86,13 +86,11 @@ int launched(hipError_t e, const char* what) {
 }
 
 int check_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
-             const w4_desc* desc, int transposed, const float* bias, const float* Y) {
+             const w4_desc* desc, int transposed) {
   int s = check_desc(desc);
   if (s != W4_OK) return s;
   if (M < 0) return fail(W4_ERR_INVALID, "M = %lld must be >= 0", (long long)M);
   if (M > ((int64_t)1 << 31) - 1) return fail(W4_ERR_UNSUPPORTED, "M must fit in int32");
-  if (M == 0) return W4_OK;
-  if (!A || !packed || !scales || !zeros || !Y) return fail(W4_ERR_INVALID, "a required pointer is NULL");
   if (desc->K % 32 != 0) return fail(W4_ERR_UNSUPPORTED, "matmul needs K %% 32 == 0 (K = %lld)", (long long)desc->K);
   if (transposed && desc->N % 8 != 0)
     return fail(W4_ERR_UNSUPPORTED, "transposed matmul needs N %% 8 == 0 (N = %lld)", (long long)desc->N);
@@ -101,21 +99,58 @@ int check_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   if (transposed && (desc->N >= ((int64_t)1 << 22) || desc->K > ((int64_t)1 << 21)))
     return fail(W4_ERR_UNSUPPORTED, "transposed matmul needs N < 2^22 and K <= 2^21 (N = %lld, K = %lld)",
                 (long long)desc->N, (long long)desc->K);
+  if (M == 0) return W4_OK;
+  if (!A || !packed || !scales || !zeros) return fail(W4_ERR_INVALID, "a required pointer is NULL");
   if (!aligned(A, 16) || !aligned(packed, 16)) return fail(W4_ERR_ALIGN, "A and packed must be 16-byte aligned");
-  if (!aligned(Y, 4) || (bias && !aligned(bias, 4)) || !aligned(scales, 2) || !aligned(zeros, 2))
-    return fail(W4_ERR_ALIGN, "Y / bias must be 4-byte and scales / zeros 2-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2)) return fail(W4_ERR_ALIGN, "scales / zeros must be 2-byte aligned");
+  return W4_OK;
+}
+
+// Output epilogue from the caller's bias, dtype and segments (validated).
+int make_epi(const w4_desc* desc, int transposed, int64_t M, const void* bias, int out_dtype, const w4_out_seg* segs,
+             int nsegs, w4::Epi* ep) {
+  if (out_dtype != W4_DT_F32 && out_dtype != W4_DT_F16 && out_dtype != W4_DT_BF16)
+    return fail(W4_ERR_INVALID, "out_dtype = %d must be F32, F16 or BF16", out_dtype);
+  if (segs == nullptr || nsegs < 1 || nsegs > w4::kMaxSegs)
+    return fail(W4_ERR_INVALID, "nsegs = %d must be in [1, %d] with a segment array", nsegs, w4::kMaxSegs);
+  const int64_t outc = transposed ? desc->K : desc->N;
+  const size_t esz = out_dtype == W4_DT_F32 ? 4 : 2;
+  int64_t c = 0;
+  for (int i = 0; i < w4::kMaxSegs; ++i) {
+    if (i < nsegs) {
+      const w4_out_seg& g = segs[i];
+      if (g.cols < 1 || g.ld < g.cols)
+        return fail(W4_ERR_INVALID, "segment %d: cols = %lld must be >= 1 and ld = %lld >= cols", i,
+                    (long long)g.cols, (long long)g.ld);
+      if (M > 0 && g.Y == nullptr) return fail(W4_ERR_INVALID, "segment %d: Y is NULL", i);
+      if (M > 0 && !aligned(g.Y, esz)) return fail(W4_ERR_ALIGN, "segment %d: Y must be %zu-byte aligned", i, esz);
+      ep->c0[i] = c;
+      ep->y[i] = g.Y;
+      ep->ld[i] = g.ld;
+      c += g.cols;
+    } else {
+      ep->c0[i] = INT64_MAX;
+      ep->y[i] = nullptr;
+      ep->ld[i] = 0;
+    }
+  }
+  if (c != outc)
+    return fail(W4_ERR_INVALID, "segment columns sum to %lld, the output has %lld", (long long)c, (long long)outc);
+  if (bias != nullptr && !aligned(bias, esz)) return fail(W4_ERR_ALIGN, "bias must be %zu-byte aligned", esz);
+  ep->bias = bias;
+  ep->dt = out_dtype;
+  ep->nseg = nsegs;
   return W4_OK;
 }
 
 w4::MmArgs make_args(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
-                     const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias, float* Y) {
+                     const uint16_t* zeros, const w4_desc* desc, int transposed, const w4::Epi& ep) {
   w4::MmArgs a;
   a.A = A;
   a.packed = packed;
   a.scales = scales;
   a.zeros = zeros;
-  a.bias = bias;
-  a.Y = Y;
+  a.ep = ep;
   a.M = M;
   a.N = desc->N;
   a.K = desc->K;
@@ -123,6 +158,16 @@ w4::MmArgs make_args(const uint16_t* A, int64_t M, const int32_t* packed, const 
   a.group = desc->mode == W4_MODE_GROUPWISE ? desc->group : (int)desc->K;
   a.transposed = transposed != 0;
   return a;
+}
+
+int run_mm(const w4::MmArgs& a, void* ws, size_t ws_bytes, void* stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (w4::gemv_supported(a, device_caps())) return launched(w4::launch_gemv(a, device_caps(), st), "gemv");
+  if (w4::gemm_lds_bytes(a, device_caps()) > device_lds_limit())
+    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a, device_caps()),
+                device_lds_limit());
+  if (ws != nullptr && !aligned(ws, 16)) return fail(W4_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return launched(w4::launch_gemm(a, device_caps(), ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
 }
 
 }  // namespace
@@ -149,8 +194,9 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
       *bytes = 0;
       if (M < 1 || M > ((int64_t)1 << 31) - 1 || desc->K % 32 != 0) break;
       static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
+      const w4::Epi ep = {};
       const w4::MmArgs a = make_args(dummy, M, reinterpret_cast<const int32_t*>(dummy), dummy, dummy, desc,
-                                     op == W4_OP_MM_T, nullptr, nullptr);
+                                     op == W4_OP_MM_T, ep);
       if (!w4::gemv_supported(a, device_caps())) *bytes = w4::gemm_workspace_bytes(a, device_caps());
       break;
     }
@@ -199,17 +245,28 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
 int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
              const w4_desc* desc, int transposed, const float* bias, float* Y, void* ws, size_t ws_bytes,
              void* stream) {
-  int s = check_mm(A, M, packed, scales, zeros, desc, transposed, bias, Y);
+  int s = check_mm(A, M, packed, scales, zeros, desc, transposed);
   if (s != W4_OK) return s;
   if (M == 0) return ok();
-  const w4::MmArgs a = make_args(A, M, packed, scales, zeros, desc, transposed, bias, Y);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (w4::gemv_supported(a, device_caps())) return launched(w4::launch_gemv(a, device_caps(), st), "gemv");
-  if (w4::gemm_lds_bytes(a, device_caps()) > device_lds_limit())
-    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a, device_caps()),
-                device_lds_limit());
-  if (ws != nullptr && !aligned(ws, 16)) return fail(W4_ERR_ALIGN, "workspace must be 16-byte aligned");
-  return launched(w4::launch_gemm(a, device_caps(), ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
+  if (Y == nullptr) return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  const int64_t outc = transposed ? desc->K : desc->N;
+  const w4_out_seg seg = {Y, outc, outc};
+  w4::Epi ep;
+  s = make_epi(desc, transposed, M, bias, W4_DT_F32, &seg, 1, &ep);
+  if (s != W4_OK) return s;
+  return run_mm(make_args(A, M, packed, scales, zeros, desc, transposed, ep), ws, ws_bytes, stream);
+}
+
+int w4a16_mm_out(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
+                 const w4_desc* desc, int transposed, const void* bias, int out_dtype, const w4_out_seg* segs,
+                 int nsegs, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_mm(A, M, packed, scales, zeros, desc, transposed);
+  if (s != W4_OK) return s;
+  w4::Epi ep;
+  s = make_epi(desc, transposed, M, bias, out_dtype, segs, nsegs, &ep);
+  if (s != W4_OK) return s;
+  if (M == 0) return ok();
+  return run_mm(make_args(A, M, packed, scales, zeros, desc, transposed, ep), ws, ws_bytes, stream);
 }
 
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
@@ -217,10 +274,10 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
   const void* p = dummy;
   int s = check_mm(static_cast<const uint16_t*>(p), M, static_cast<const int32_t*>(p), dummy, dummy, desc,
-                   transposed, nullptr, reinterpret_cast<const float*>(p));
+                   transposed);
   if (s != W4_OK || M == 0) return nullptr;
-  const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, nullptr,
-                                 nullptr);
+  const w4::Epi ep = {};
+  const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, ep);
   if (w4::gemv_supported(a, device_caps())) return w4::gemv_name(a);
   return w4::gemm_name(a, device_caps(), true);
 }

@@ -33,6 +33,7 @@
 //     of A, column (l % 32) and the same slots of B; result register r of a 32x32
 //     block is row 8 (r / 4) + 4 (l / 32) + (r % 4) of column l % 32.
 #include "common.h"
+#include "epilogue.h"
 #include "launch.h"
 
 #include <algorithm>
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const uint16_t* __restrict__ zeros,
-                                                            const float* __restrict__ bias, float* __restrict__ Y,
+                                                            const Epi ep,
                                                             int M, int N, int K, int log2g, int kt_per_slice,
                                                             float* __restrict__ part) {
   constexpr int T = WM * WN * 64;
@@ -476,38 +477,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     }
   }
 
-  // ---- epilogue: bias in fp32, masked fp32 stores.  Result register r of a 32x32
-  // block sits at row 8 (r / 4) + 4 (lane / 32) + (r % 4), column lane % 32.  A split-K
-  // slice writes its partial sums (no bias) to its own [M][OUTC] plane of `part`.
-  float* out = part != nullptr ? part + (size_t)blockIdx.z * M * OUTC : Y;
-  const float* bz = part != nullptr ? nullptr : bias;
+  // ---- epilogue.  Result register r of a 32x32 block sits at row 8 (r / 4) +
+  // 4 (lane / 32) + (r % 4), column lane % 32.  A split-K slice writes its partial sums
+  // (fp32, no bias) to its own [M][OUTC] plane of `part`; an unsplit launch stores
+  // through the output epilogue (bias, output dtype, output segments).
   const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
   const int cbase = c0 + wn * FN * 32 + lr;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = cbase + j * 32;
     if (c >= OUTC) continue;
-    const float b = bz != nullptr ? bz[c] : 0.0f;
+    if (part != nullptr) {
+      float* out = part + (size_t)blockIdx.z * M * OUTC;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-        if (m < M) out[(size_t)m * OUTC + c] = acc[i][j][r] + b;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
+          if (m < M) out[(size_t)m * OUTC + c] = acc[i][j][r];
+        }
+    } else {
+      const EpiCol col = epi_col(ep, c);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
+          if (m < M) epi_put(ep, col, m, acc[i][j][r]);
+        }
     }
   }
 }
 
-// Split-K reduction: Y = sum over the S partial planes (fixed order) + bias.
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t total,
-                                                            int outc, const float* __restrict__ bias,
-                                                            float* __restrict__ Y) {
+// Split-K reduction: output = epilogue(sum over the S partial [M][outc] planes, in a
+// fixed order).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
+                                                            int64_t outc, const Epi ep) {
+  const int64_t total = M * outc;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     float v = part[i];
     for (int s = 1; s < S; ++s) v += part[(size_t)s * total + i];
-    if (bias != nullptr) v += bias[i % outc];
-    Y[i] = v;
+    const int64_t m = i / outc, c = i - m * outc;
+    epi_put(ep, epi_col(ep, c), m, v);
   }
 }
 
@@ -631,11 +642,11 @@ hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
   splits = (kt_all + kts - 1) / kts;  // every slice gets at least one contraction step
   const dim3 grid((unsigned)((outc + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
   const int log2g = 31 - __builtin_clz((unsigned)a.group);
-  k<<<grid, WM * WN * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.M, (int)a.N, (int)a.K,
+  k<<<grid, WM * WN * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K,
                                       log2g, kts, splits > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, a.M * outc, (int)outc, a.bias, a.Y, st);
+  return launch_splitk_reduce(part, splits, a.M, outc, a.ep, st);
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>
@@ -667,10 +678,10 @@ hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t total, int outc, const float* bias, float* Y,
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t outc, const Epi& ep,
                                 hipStream_t st) {
-  const int64_t blocks = (total + 255) / 256;
-  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, total, outc, bias, Y);
+  const int64_t blocks = (M * outc + 255) / 256;
+  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, outc, ep);
   return hipGetLastError();
 }
 

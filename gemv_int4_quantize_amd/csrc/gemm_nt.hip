@@ -28,6 +28,7 @@
 //   * split-K: blockIdx.z takes a contiguous range of steps and writes fp32 partial sums
 //     to its own plane; a separate kernel sums the planes in a fixed order.
 #include "common.h"
+#include "epilogue.h"
 #include "launch.h"
 
 namespace w4 {
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros,
-                                                         const float* __restrict__ bias, float* __restrict__ Y,
+                                                         const Epi ep,
                                                          int M, int N, int K, int meta_row, int log2g,
                                                          int kt_per_slice, float* __restrict__ part) {
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
@@ -272,22 +273,32 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 
   // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
-  // lr; a split-K slice writes its partial sums (no bias) to its own [M][N] plane
-  float* out = part != nullptr ? part + (size_t)blockIdx.z * M * N : Y;
-  const float* bz = part != nullptr ? nullptr : bias;
+  // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][N] plane,
+  // an unsplit launch stores through the output epilogue
   const int rbase = m0 + h * 4;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = n0w + j * 32 + lr;
     if (c >= N) continue;
-    const float b = bz != nullptr ? bz[c] : 0.0f;
+    if (part != nullptr) {
+      float* out = part + (size_t)blockIdx.z * M * N;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-        if (m < M) out[(size_t)m * N + c] = acc[i][j][r] + b;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
+          if (m < M) out[(size_t)m * N + c] = acc[i][j][r];
+        }
+    } else {
+      const EpiCol col = epi_col(ep, c);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
+          if (m < M) epi_put(ep, col, m, acc[i][j][r]);
+        }
+    }
   }
 }
 
@@ -307,11 +318,11 @@ hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) 
   const int meta_row = a.mode == W4_MODE_GLOBAL ? 0 : a.mode == W4_MODE_ROWWISE ? 1 : (int)(a.K / a.group);
   const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
   const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
-  k<<<grid, 256, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.M, (int)a.N, (int)a.K, meta_row,
+  k<<<grid, 256, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K, meta_row,
                             log2g, kts, splits > 1 ? part : nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, a.M * a.N, (int)a.N, a.bias, a.Y, st);
+  return launch_splitk_reduce(part, splits, a.M, a.N, a.ep, st);
 }
 
 template <int FM, int FN, bool KTAIL>

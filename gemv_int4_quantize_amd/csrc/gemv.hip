@@ -18,12 +18,13 @@
 //     rounding by v_cvt_pk_bf16_f32, products by v_dot2_f32_bf16;
 //   * the R*M partial sums of a row group are reduced across the wave with a
 //     transposing butterfly on v_permlane32_swap / v_permlane16_swap and DPP row
-//     moves (no LDS round trips), parked in LDS, and written out coalesced with the
-//     bias at the end.
+//     moves (no LDS round trips), parked in LDS, and written out at the end through
+//     the output epilogue (bias, output dtype, output segments).
 #include <algorithm>
 #include <atomic>
 
 #include "common.h"
+#include "epilogue.h"
 #include "launch.h"
 
 namespace w4 {
@@ -124,14 +125,32 @@ constexpr int kWaves = 16;
 
 // meta_row: (scale, zero) pairs per row (K / g, 1 for ROWWISE, 0 for GLOBAL);
 // log2g: group shift (31 for ROWWISE / GLOBAL, so every column maps to pair 0 of its row).
-template <int M, int R, int GPC>
+// Output argument: the general epilogue (output dtype, bias dtype, segments) when GEN, else
+// just the fp32 bias and Y [M][N] pointers -- a 64-byte argument block instead of 160,
+// which measurably shortens these few-microsecond launches.
+struct PlainOut {
+  const float* bias;
+  float* Y;
+};
+template <bool GEN>
+struct OutArg {
+  typedef PlainOut type;
+};
+template <>
+struct OutArg<true> {
+  typedef Epi type;
+};
+
+template <int M, int R, int GPC, bool GEN>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __restrict__ X,
                                                            const int32_t* __restrict__ packed,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ zeros,
-                                                           const float* __restrict__ bias, float* __restrict__ Y,
-                                                           int N, int K, int meta_row, int log2g, int rows_per_block,
-                                                           int phase_iters) {
+                                                           const typename OutArg<GEN>::type ep,
+                                                           int N, int K, int meta_row, int geo) {
+  // geo packs log2g (bits 0-4), rows_per_block (5-15) and phase_iters (16-30): with the
+  // plain output the whole argument block is one 64-byte line
+  const int log2g = geo & 31, rows_per_block = (geo >> 5) & 2047, phase_iters = geo >> 16;
   extern __shared__ u32x4 smem[];
   constexpr int T = kWaves * 64;
   const int KS = K >> 5;               // 16-byte chunks per row
@@ -272,10 +291,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
   }
 
   __syncthreads();
-  for (int u = tid; u < (r1 - r0) * M; u += T) {
-    const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
-    const int n = r0 + lr;
-    Y[(size_t)m * N + n] = outs[lr * M + m] + (bias != nullptr ? bias[n] : 0.0f);
+  if constexpr (!GEN) {
+    float* Y = ep.Y;
+    const float* bias = ep.bias;
+    for (int u = tid; u < (r1 - r0) * M; u += T) {
+      const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
+      const int n = r0 + lr;
+      Y[(size_t)m * N + n] = outs[lr * M + m] + (bias != nullptr ? bias[n] : 0.0f);
+    }
+  } else {
+    for (int u = tid; u < (r1 - r0) * M; u += T) {
+      const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
+      const int n = r0 + lr;
+      epi_put(ep, epi_col(ep, n), m, outs[lr * M + m]);
+    }
   }
 }
 
@@ -311,9 +340,9 @@ int meta_row(const MmArgs& a) {
   return (int)(a.K / a.group);
 }
 
-template <int M, int R, int GPC>
+template <int M, int R, int GPC, bool GEN>
 hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  auto k = gemv_kernel<M, R, GPC>;
+  auto k = gemv_kernel<M, R, GPC, GEN>;
   static std::atomic<int> lds_set{64 * 1024};  // largest dynamic LDS size enabled so far
   if ((int)p.lds > lds_set.load()) {
     const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
@@ -321,16 +350,26 @@ hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
     lds_set.store((int)p.lds);
   }
   const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
-  k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.bias, a.Y, (int)a.N, (int)a.K,
-                                           meta_row(a), log2g, p.rows_per_block, p.phase_iters);
+  typename OutArg<GEN>::type out;
+  if constexpr (GEN) out = a.ep;
+  else out = PlainOut{static_cast<const float*>(a.ep.bias), static_cast<float*>(a.ep.y[0])};
+  k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, out, (int)a.N, (int)a.K,
+                                           meta_row(a), log2g | (p.rows_per_block << 5) | (p.phase_iters << 16));
   return hipGetLastError();
+}
+
+template <int M, bool GEN>
+hipError_t run_g(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
+  const bool g16 = a.mode == W4_MODE_GROUPWISE && a.group == 16;  // two groups per 32-code chunk
+  if (p.R == 2) return g16 ? run<M, 2, 2, GEN>(a, p, st) : run<M, 2, 1, GEN>(a, p, st);
+  return g16 ? run<M, 1, 2, GEN>(a, p, st) : run<M, 1, 1, GEN>(a, p, st);
 }
 
 template <int M>
 hipError_t run_m(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  const bool g16 = a.mode == W4_MODE_GROUPWISE && a.group == 16;  // two groups per 32-code chunk
-  if (p.R == 2) return g16 ? run<M, 2, 2>(a, p, st) : run<M, 2, 1>(a, p, st);
-  return g16 ? run<M, 1, 2>(a, p, st) : run<M, 1, 1>(a, p, st);
+  const Epi& e = a.ep;
+  const bool plain = e.nseg == 1 && e.dt == W4_DT_F32 && e.ld[0] == a.N;
+  return plain ? run_g<M, false>(a, p, st) : run_g<M, true>(a, p, st);
 }
 
 }  // namespace

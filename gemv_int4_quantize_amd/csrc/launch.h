@@ -17,14 +17,26 @@ size_t quantize_workspace_bytes(int mode);
 hipError_t launch_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros, int64_t N,
                              int64_t K, int mode, int g, void* out, int out_dt, hipStream_t st);
 
+// Output epilogue of a matmul (passed to the kernels by value): output column c of
+// row m gets out_rne(acc + bias[c]) in dtype dt, stored in the segment s holding c at
+// y[s] + m * ld[s] + (c - c0[s]).  The bias, when present, has the output dtype.
+constexpr int kMaxSegs = 4;
+struct Epi {
+  const void* bias;             // nullptr or [outc] elements of dt
+  int dt;                       // W4_DT_F32, W4_DT_F16 or W4_DT_BF16
+  int nseg;                     // 1 .. kMaxSegs
+  int64_t c0[kMaxSegs];         // first column of each segment (INT64_MAX past nseg)
+  void* y[kMaxSegs];
+  int64_t ld[kMaxSegs];         // row stride of each segment, in elements
+};
+
 // Matmul problem after validation: A [M][L] bf16 (L = contraction), packed [N][K/8].
 struct MmArgs {
   const uint16_t* A;
   const int32_t* packed;
   const uint16_t* scales;
   const uint16_t* zeros;
-  const float* bias;
-  float* Y;
+  Epi ep;
   int64_t M, N, K;
   int mode;   // w4_mode
   int group;  // GROUPWISE g, else K
@@ -57,8 +69,8 @@ hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t
 bool gemm_nt_reg_supported(const MmArgs& a);
 hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st);
 
-// Y = sum of `splits` fp32 planes of `total` values (fixed order) + bias[i % outc].
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t total, int outc, const float* bias, float* Y,
+// Output = epilogue(sum of `splits` fp32 [M][outc] planes, in a fixed order).
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t outc, const Epi& ep,
                                 hipStream_t st);
 
 }  // namespace w4

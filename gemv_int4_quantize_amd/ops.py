@@ -157,36 +157,78 @@ def dequantize(qw: QuantizedWeight, dtype=torch.bfloat16) -> torch.Tensor:
     return out
 
 
-def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: torch.Tensor | None = None,
-       out: torch.Tensor | None = None, split_k: bool = True) -> torch.Tensor:
-    """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias); fp32 output.
+_ODT = {torch.float32: DT_F32, torch.float16: DT_F16, torch.bfloat16: DT_BF16}
 
-    split_k lets a GEMM with few output tiles split its contraction over a workspace
-    (allocated here from torch's caching allocator; the sum order is fixed)."""
+
+def _workspace(qw: QuantizedWeight, M: int, transposed: bool, split_k: bool, device):
+    ws_bytes = ctypes.c_size_t(0)
+    if split_k:
+        op = _lib.OP_MM_T if transposed else _lib.OP_MM
+        check(lib().w4_workspace_bytes(ctypes.byref(qw.desc()), op, M, ctypes.byref(ws_bytes)))
+    ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=device) if ws_bytes.value else None
+    return ws, ws_bytes.value
+
+
+def _mm_out(a: torch.Tensor, qw: QuantizedWeight, transposed: bool, bias, outs, split_k: bool):
+    """Marshal one w4a16_mm_out call: `outs` are 2-D [M][cols_i] tensors of one dtype
+    (rows contiguous, any row stride) covering the output columns in order."""
     a = _as_bf16(a)
-    _need_cuda(a, qw.packed, bias, out)
+    _need_cuda(a, qw.packed, bias, *outs)
     if a.dim() != 2 or not a.is_contiguous():
         raise ValueError("activations must be a contiguous 2-D tensor")
     M, L = a.shape
     if L != (qw.N if transposed else qw.K):
         raise ValueError(f"activation width {L} does not match the weight ({qw.N}x{qw.K}, transposed={transposed})")
+    dt = outs[0].dtype
+    if dt not in _ODT or any(o.dtype != dt for o in outs):
+        raise ValueError("outputs must share one dtype among float32, float16 and bfloat16")
     outc = qw.K if transposed else qw.N
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != outc or not bias.is_contiguous()):
-        raise ValueError(f"bias must be a contiguous fp32 vector of length {outc}")
-    if out is None:
-        out = torch.empty((M, outc), dtype=torch.float32, device=a.device)
-    elif out.shape != (M, outc) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp32 tensor of the output shape")
+    if bias is not None and (bias.dtype != dt or bias.numel() != outc or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous {dt} vector of length {outc}")
+    segs = (_lib.W4OutSeg * len(outs))()
+    for i, o in enumerate(outs):
+        if o.dim() != 2 or o.shape[0] != M or o.stride(1) != 1:
+            raise ValueError("each output must be a 2-D [M][cols] tensor with contiguous rows")
+        segs[i].Y = o.data_ptr()
+        segs[i].cols = o.shape[1]
+        segs[i].ld = o.stride(0) if M > 1 else o.shape[1]
+    ws, ws_bytes = _workspace(qw, M, transposed, split_k, a.device)
     desc = qw.desc()
-    op = _lib.OP_MM_T if transposed else _lib.OP_MM
-    ws_bytes = ctypes.c_size_t(0)
-    if split_k:
-        check(lib().w4_workspace_bytes(ctypes.byref(desc), op, M, ctypes.byref(ws_bytes)))
-    ws = torch.empty(ws_bytes.value, dtype=torch.uint8, device=a.device) if ws_bytes.value else None
-    check(lib().w4a16_mm(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
-                         1 if transposed else 0, _ptr(bias), _ptr(out), _ptr(ws), ws_bytes.value,
-                         _stream(a.device)))
+    check(lib().w4a16_mm_out(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
+                             1 if transposed else 0, _ptr(bias), _ODT[dt], segs, len(outs), _ptr(ws), ws_bytes,
+                             _stream(a.device)))
+
+
+def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: torch.Tensor | None = None,
+       out: torch.Tensor | None = None, split_k: bool = True, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias), fp32 accumulation.
+
+    The output is fp32 unless `out_dtype` (or `out`) asks for bfloat16 / float16, rounded once
+    to nearest even; the bias, when given, has the output dtype.  split_k lets a GEMM with few
+    output tiles split its contraction over a workspace (allocated here from torch's caching
+    allocator; the sum order is fixed)."""
+    a = _as_bf16(a)
+    M = a.shape[0] if a.dim() == 2 else -1
+    outc = qw.K if transposed else qw.N
+    dt = out_dtype if out_dtype is not None else (out.dtype if out is not None else torch.float32)
+    if out is None:
+        out = torch.empty((max(M, 0), outc), dtype=dt, device=a.device)
+    elif out.shape != (M, outc) or out.dtype != dt or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of the output shape and dtype")
+    _mm_out(a, qw, transposed, bias, [out], split_k)
     return out
+
+
+def mm_split(a: torch.Tensor, qw: QuantizedWeight, outs: list[torch.Tensor], bias: torch.Tensor | None = None,
+             transposed: bool = False, split_k: bool = True) -> list[torch.Tensor]:
+    """One product written to separate outputs in one launch: outs[i] [M][n_i] receives the
+    next n_i output columns (for a fused Q/K/V weight, non-transposed: Q, K and V).
+    Outputs share a dtype (fp32, bf16 or fp16) and may be row-strided views; the bias, if
+    any, spans all output columns in that dtype."""
+    if sum(o.shape[1] for o in outs) != (qw.K if transposed else qw.N):
+        raise ValueError("the outputs' columns must sum to the output width")
+    _mm_out(a, qw, transposed, bias, list(outs), split_k)
+    return list(outs)
 
 
 def kernel_for(M: int, N: int, K: int, mode="groupwise", group: int | None = 128, transposed=False) -> str | None:

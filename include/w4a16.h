@@ -18,8 +18,9 @@
  *   scales  fp16 bits: GLOBAL [1], ROWWISE [N], GROUPWISE [N][K/g] (group fastest).
  *   zeros   fp16 bits, same shape as scales.
  *   A       bf16 bits: X [M][K] (non-transposed) or dY [M][N] (transposed).
- *   Y       fp32: [M][N] (non-transposed) or [M][K] (transposed).
- *   bias    fp32, optional: length N (non-transposed) or K (transposed).
+ *   Y       fp32: [M][N] (non-transposed) or [M][K] (transposed); w4a16_mm_out
+ *           also writes bf16 / fp16 and splits the columns over up to 4 outputs.
+ *   bias    optional, in the output dtype: length N (non-transposed) or K (transposed).
  *
  * Arithmetic:
  *   s = fp16_rne((max - min) / 15) per group, replaced by 1 when it is 0 or not
@@ -120,6 +121,33 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
 int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
              const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias,
              float* Y, void* ws, size_t ws_bytes, void* stream);
+
+/* One output segment of w4a16_mm_out: it receives the next `cols` output columns
+ * (segments cover the output columns in order), column j of the segment at row m
+ * being Y[m * ld + j] in the call's out_dtype.  Y device pointer, ld >= cols. */
+typedef struct {
+  void* Y;
+  int64_t cols;
+  int64_t ld;
+} w4_out_seg;
+
+/* w4a16_mm with the output epilogue spelled out:
+ *   out = out_rne(acc + bias[c]) for output column c, acc the fp32 sum;
+ *   out_dtype W4_DT_F32, W4_DT_BF16 or W4_DT_F16 (round to nearest even);
+ *   bias NULL or outc values (N non-transposed, K transposed) in out_dtype,
+ *   converted exactly to fp32 and added before the one rounding;
+ *   segs[0 .. nsegs-1], 1 <= nsegs <= 4, split the outc output columns, so a
+ *   fused Q/K/V weight writes Q, K and V to separate tensors in one launch.
+ * The segment columns must sum to outc; each Y and the bias must be aligned to
+ * the element size.  Everything else (operands, workspace, stream, errors) is
+ * as for w4a16_mm, which equals this call with W4_DT_F32 and one segment of
+ * ld = outc.  Sources: "[Kernel] Adding bias epilogue support for
+ * cutlass_scaled_mm" (vLLM #5560: the bias in the output dtype); "Add fused QKV
+ * HQQ triton_mm test" (pytorch/ao #306: one fused Q/K/V product). */
+int w4a16_mm_out(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
+                 const uint16_t* zeros, const w4_desc* desc, int transposed, const void* bias,
+                 int out_dtype, const w4_out_seg* segs, int nsegs, void* ws, size_t ws_bytes,
+                 void* stream);
 
 /* Name of the kernel w4a16_mm would launch for these arguments ("gemv_m4",
  * "gemm_nt_256x128", "gemm_t_256x256_splitk4", ...) given the workspace

@@ -45,6 +45,8 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
 * matmul: exact-rational triple loop on tiny shapes, one-hot pins of the layout
   in both modes, constant-code closed form, linearity and bias.
 * fused QKV: column concatenation (non-transposed) and sum (transposed).
+* round_output: hand-derived bf16 / fp16 roundings (ties to even, 8 and 11
+  significant bits, the fp16 maximum).
 * compression: the page's printed column reproduced by its closed form.
 * MAE: parity unpinned (the page's data distribution is unstated); only its
   trends are checked.
@@ -58,7 +60,7 @@ __all__ = [
     "GLOBAL", "ROWWISE", "GROUPWISE", "MODE_NAMES",
     "meta_shape", "to_f32", "quantize", "pack", "unpack", "quantize_pack",
     "dequantize_f32", "bf16_rne_bits", "bf16_bits_to_f64", "dequantize_bf16_bits",
-    "matmul", "fuse_rows", "mae", "compression_ratio", "page_compression_ratio",
+    "matmul", "round_output", "fuse_rows", "mae", "compression_ratio", "page_compression_ratio",
 ]
 
 GLOBAL, ROWWISE, GROUPWISE = 0, 1, 2
@@ -225,6 +227,26 @@ def matmul(a_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
     return y
+
+
+def round_output(y: np.ndarray, dtype: str) -> np.ndarray:
+    """The matmul output in its storage dtype, as float64.
+
+    "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560) gives
+    the bias the output dtype and adds it before the one conversion of the sum to
+    that dtype.  Here the sum (bias included, see ``matmul``) is rounded to fp32 and
+    then to ``dtype`` ("f32", "bf16" or "f16"), round to nearest, ties to even; the
+    fp32 step only differs from a direct rounding on exact double-rounding ties.
+    """
+    y32 = np.asarray(y, dtype=np.float64).astype(_F32)
+    if dtype == "f32":
+        return y32.astype(np.float64)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(bf16_rne_bits(y32))
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return y32.astype(np.float16).astype(np.float64)
+    raise ValueError(dtype)
 
 
 def fuse_rows(parts):

@@ -136,3 +136,30 @@ def test_dispatch_names():
     assert w4.kernel_for(2048, 12288, 4096, "groupwise", 64, transposed=True).startswith("gemm_t_")
     assert w4.kernel_for(4, 4096, 4096, "groupwise", 128, transposed=True).startswith("gemm_t_")
     assert w4.kernel_for(4, 4096, 40, "rowwise", None) is None
+
+
+def test_mm_out_validation_before_launch():
+    """w4a16_mm_out rejects bad output specifications before touching any pointer."""
+    L = _lib.lib()
+    d = _lib.W4Desc(64, 128, _lib.MODE_ROWWISE, 0)
+    a16 = ctypes.c_void_p(0x10000)
+
+    def call(segs, nsegs, dt=_lib.DT_BF16, M=4, bias=None, transposed=0):
+        arr = (_lib.W4OutSeg * max(1, len(segs)))(*[_lib.W4OutSeg(*s) for s in segs]) if segs else None
+        return L.w4a16_mm_out(a16, M, a16, a16, a16, ctypes.byref(d), transposed, bias, dt, arr, nsegs,
+                              None, 0, None)
+
+    ok3 = [(0x20000, 32, 32), (0x30000, 16, 16), (0x40000, 16, 20)]
+    assert call(ok3, 3, dt=7) == _lib.W4_ERR_INVALID                       # unknown dtype
+    assert call(ok3, 0) == _lib.W4_ERR_INVALID                             # no segments
+    assert call(ok3 + [(0x50000, 1, 1)] * 2, 5) == _lib.W4_ERR_INVALID     # more than four
+    assert call([(0x20000, 32, 32), (0x30000, 16, 16)], 2) == _lib.W4_ERR_INVALID  # 48 != N
+    assert call([(0x20000, 64, 63)], 1) == _lib.W4_ERR_INVALID             # ld < cols
+    assert call([(0x20000, 0, 0), (0x30000, 64, 64)], 2) == _lib.W4_ERR_INVALID    # empty segment
+    assert call([(0x20001, 64, 64)], 1) == _lib.W4_ERR_ALIGN               # bf16 output at an odd address
+    assert call([(0x20002, 64, 64)], 1, dt=_lib.DT_F32) == _lib.W4_ERR_ALIGN  # fp32 needs 4 bytes
+    assert call([(0x20000, 64, 64)], 1, bias=ctypes.c_void_p(0x60001)) == _lib.W4_ERR_ALIGN
+    assert call([(None, 64, 64)], 1) == _lib.W4_ERR_INVALID                # NULL output
+    # M == 0: structure still checked, pointers never touched
+    assert call([(None, 64, 64)], 1, M=0) == _lib.W4_OK
+    assert call([(None, 32, 32)], 1, M=0) == _lib.W4_ERR_INVALID

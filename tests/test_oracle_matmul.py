@@ -126,3 +126,24 @@ def test_fuse_rejects_global():
     parts = [O.quantize_pack(synth.weight(206, i, 8, K, "f32"), O.GLOBAL) for i in range(3)]
     with pytest.raises(ValueError):
         O.fuse_rows(parts)
+
+
+def test_round_output_pins():
+    """Output rounding of the epilogue: values whose bf16 / fp16 roundings follow from the
+    formats' definitions (8 and 11 significant bits, ties to even)."""
+    y = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, 1.0 + 2.0**-8 + 2.0**-20, -3.0 - 2.0**-7,
+                  65504.0, 1e-3])
+    # bf16: 1 + 2^-8 is the tie between 1 and 1 + 2^-7 -> even (1); 1 + 3*2^-8 ties -> 1 + 2^-6;
+    # just above the tie rounds up; -3 - 2^-7 ties between -3 and -3 - 2^-6 -> even (-3)
+    want_bf16 = [1.0, 1.0, 1.0 + 2.0**-6, 1.0 + 2.0**-7, -3.0, 65536.0, None]
+    got = O.round_output(y, "bf16")
+    for g, w in zip(got, want_bf16):
+        if w is not None:
+            assert g == w
+    # 1e-3 in bf16: the nearest 8-bit significand times 2^-10 (1e-3 = 1.024 * 2^-10)
+    assert got[-1] == round(1.024 * 128) / 128 * 2.0**-10
+    # fp16 keeps 1 + 2^-8 (11 significant bits) and tops out at 65504
+    got16 = O.round_output(y, "f16")
+    assert got16[1] == 1.0 + 2.0**-8 and got16[5] == 65504.0
+    assert got16[3] == 1.0 + 2.0**-8  # 2^-20 is below half an fp16 ulp at 1
+    np.testing.assert_array_equal(O.round_output(y, "f32"), y.astype(np.float32).astype(np.float64))
