@@ -21,10 +21,11 @@ W4_ERR_LAUNCH = -5
 MODE_GLOBAL, MODE_ROWWISE, MODE_GROUPWISE = 0, 1, 2
 DT_F32, DT_F16, DT_BF16 = 0, 1, 2
 OP_QUANTIZE, OP_MM, OP_MM_T, OP_DEQUANTIZE = 0, 1, 2, 3
+ZERO_FP16, ZERO_INT = 0, 1
 
 # every entry point declared in include/w4a16.h
 EXPORTS = (
-    "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_dequantize", "w4a16_mm",
+    "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize", "w4a16_mm",
     "w4a16_mm_out", "w4a16_mm_kernel", "w4_status_string", "w4_last_error", "w4_version",
 )
 
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
     L.w4_meta_pairs.argtypes = [pdesc, ctypes.POINTER(ctypes.c_int64)]
     L.w4_workspace_bytes.argtypes = [pdesc, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
     L.w4_quantize_pack.argtypes = [vp, i32, pdesc, vp, vp, vp, vp, sz, vp]
+    L.w4_quantize_pack_zp.argtypes = [vp, i32, pdesc, i32, vp, vp, vp, vp, sz, vp]
     L.w4_dequantize.argtypes = [vp, vp, vp, pdesc, vp, i32, vp]
     L.w4a16_mm.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp, sz, vp]
     L.w4a16_mm_out.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz, vp]
@@ -74,8 +76,8 @@ def lib() -> ctypes.CDLL:
     L.w4_last_error.restype = ctypes.c_char_p
     L.w4_version.argtypes = []
     L.w4_version.restype = ctypes.c_char_p
-    for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_dequantize", "w4a16_mm",
-                 "w4a16_mm_out"):
+    for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize",
+                 "w4a16_mm", "w4a16_mm_out"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -205,12 +205,14 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes) {
   return ok();
 }
 
-int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc, int32_t* packed, uint16_t* scales,
-                     uint16_t* zeros, void* ws, size_t ws_bytes, void* stream) {
+int w4_quantize_pack_zp(const void* W, int w_dtype, const w4_desc* desc, int zero_kind, int32_t* packed,
+                        uint16_t* scales, uint16_t* zeros, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(desc);
   if (s != W4_OK) return s;
   if (w_dtype != W4_DT_F32 && w_dtype != W4_DT_F16 && w_dtype != W4_DT_BF16)
     return fail(W4_ERR_INVALID, "w_dtype = %d is not F32, F16 or BF16", w_dtype);
+  if (zero_kind != W4_ZERO_FP16 && zero_kind != W4_ZERO_INT)
+    return fail(W4_ERR_INVALID, "zero_kind = %d is not W4_ZERO_FP16 or W4_ZERO_INT", zero_kind);
   if (!W || !packed || !scales || !zeros) return fail(W4_ERR_INVALID, "a required pointer is NULL");
   if (!aligned(W, 16)) return fail(W4_ERR_ALIGN, "W must be 16-byte aligned");
   if (!aligned(packed, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
@@ -222,9 +224,14 @@ int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc, int32_t* p
     if (!aligned(ws, 8)) return fail(W4_ERR_ALIGN, "workspace must be 8-byte aligned");
   }
   const int g = desc->mode == W4_MODE_GROUPWISE ? desc->group : (int)desc->K;
-  return launched(w4::launch_quantize(W, w_dtype, desc->N, desc->K, desc->mode, g, packed, scales, zeros, ws,
-                                      static_cast<hipStream_t>(stream)),
+  return launched(w4::launch_quantize(W, w_dtype, desc->N, desc->K, desc->mode, g, zero_kind == W4_ZERO_INT, packed,
+                                      scales, zeros, ws, static_cast<hipStream_t>(stream)),
                   "quantize_pack");
+}
+
+int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc, int32_t* packed, uint16_t* scales,
+                     uint16_t* zeros, void* ws, size_t ws_bytes, void* stream) {
+  return w4_quantize_pack_zp(W, w_dtype, desc, W4_ZERO_FP16, packed, scales, zeros, ws, ws_bytes, stream);
 }
 
 int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros, const w4_desc* desc,

@@ -10,7 +10,8 @@
 
 namespace w4 {
 
-hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+// intz: integer zero points (z = clamp(rint(-min / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15))
+hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int intz, int32_t* packed,
                            uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st);
 size_t quantize_workspace_bytes(int mode);
 

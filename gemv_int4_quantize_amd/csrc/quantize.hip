@@ -7,6 +7,11 @@
 //             z = fp16_rne((0 - min) / s),
 //             q = clamp(rint(w / s + z), 0, 15),
 // every step in IEEE fp32 (correctly rounded division, no contraction).
+// Integer zero points, in the AWQ style of the W4A16 AWQ g = 128 workload of "Modify
+// small-batched weight only quantization" (TensorRT-LLM #2213):
+//             z = clamp(rint((0 - min) / s), 0, 15)  (an integer, exact in fp16),
+//             q = clamp(rint(w / s) + z, 0, 15),
+// so that q - z is an integer and the dequantized weight is exactly (q - z) * s.
 //
 // The kernels are HBM streams: each lane reads the 8 elements of one output word
 // with 16-byte loads (32 for fp32) and writes one int32 word.
@@ -44,7 +49,7 @@ struct QParams {
   uint16_t sb, zb;   // their fp16 bits
 };
 
-__device__ __forceinline__ QParams qparams(float lo, float hi) {
+__device__ __forceinline__ QParams qparams(float lo, float hi, bool intz) {
   const float s32 = (hi - lo) / 15.0f;
   uint16_t sb = f32_to_f16_bits(s32);
   float s = f16_bits_to_f32(sb);
@@ -56,7 +61,8 @@ __device__ __forceinline__ QParams qparams(float lo, float hi) {
   // backend turns `0.0f - lo` into a negate modifier, which yields -0 for lo == +0.
   const float nlo = lo == 0.0f ? 0.0f : -lo;
   const float z32 = nlo / s;
-  const uint16_t zb = f32_to_f16_bits(z32);
+  const uint16_t zb = intz ? f32_to_f16_bits(__builtin_fminf(__builtin_fmaxf(__builtin_rintf(z32), 0.0f), 15.0f))
+                           : f32_to_f16_bits(z32);
   QParams p;
   p.s = s;
   p.z = f16_bits_to_f32(zb);
@@ -65,16 +71,16 @@ __device__ __forceinline__ QParams qparams(float lo, float hi) {
   return p;
 }
 
-__device__ __forceinline__ uint32_t code4(float w, const QParams& p) {
-  const float t = w / p.s + p.z;  // IEEE divide, then add
-  const float r = __builtin_rintf(t);  // round half to even
+__device__ __forceinline__ uint32_t code4(float w, const QParams& p, bool intz) {
+  // fp16 zero: rint(w / s + z); integer zero: rint(w / s) + z (the add is then exact)
+  const float r = intz ? __builtin_rintf(w / p.s) + p.z : __builtin_rintf(w / p.s + p.z);  // half to even
   return (uint32_t)__builtin_fminf(__builtin_fmaxf(r, 0.0f), 15.0f);
 }
 
-__device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p) {
+__device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p, bool intz) {
   uint32_t w = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w |= code4(v[j], p) << (4 * j);
+  for (int j = 0; j < 8; ++j) w |= code4(v[j], p, intz) << (4 * j);
   return w;
 }
 
@@ -83,7 +89,8 @@ __device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p) {
 template <int DT, int T>
 __global__ __launch_bounds__(256) void quant_small_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
                                                           uint16_t* __restrict__ scales,
-                                                          uint16_t* __restrict__ zeros, int64_t total_words) {
+                                                          uint16_t* __restrict__ zeros, int64_t total_words,
+                                                          int intz) {
   const int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool valid = gw < total_words;
   float v[8];
@@ -104,8 +111,8 @@ __global__ __launch_bounds__(256) void quant_small_kernel(const void* __restrict
     lo = __builtin_fminf(lo, __shfl_xor(lo, o));
     hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
   }
-  const QParams p = qparams(lo, hi);
-  const uint32_t word = pack8(v, p);
+  const QParams p = qparams(lo, hi, intz != 0);
+  const uint32_t word = pack8(v, p, intz != 0);
   if (valid) {
     packed[gw] = (int32_t)word;
     if ((threadIdx.x & (T - 1)) == 0) {
@@ -121,7 +128,7 @@ template <int DT>
 __global__ __launch_bounds__(256) void quant_large_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
                                                           uint16_t* __restrict__ scales,
                                                           uint16_t* __restrict__ zeros, int64_t num_groups,
-                                                          int wpg) {
+                                                          int wpg, int intz) {
   const int lane = threadIdx.x & 63;
   const int64_t grp = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (grp >= num_groups) return;
@@ -141,11 +148,11 @@ __global__ __launch_bounds__(256) void quant_large_kernel(const void* __restrict
     lo = __builtin_fminf(lo, __shfl_xor(lo, o));
     hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
   }
-  const QParams p = qparams(lo, hi);
+  const QParams p = qparams(lo, hi, intz != 0);
   for (int c = lane; c < wpg; c += kWave) {
     float v[8];
     load8<DT>(W, (w0 + c) * 8, v);
-    packed[w0 + c] = (int32_t)pack8(v, p);
+    packed[w0 + c] = (int32_t)pack8(v, p, intz != 0);
   }
   if (lane == 0) {
     scales[grp] = p.sb;
@@ -199,18 +206,18 @@ template <int DT>
 __global__ __launch_bounds__(256) void quant_global_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
                                                            uint16_t* __restrict__ scales,
                                                            uint16_t* __restrict__ zeros, int64_t total_words,
-                                                           const float* __restrict__ partial, int nparts) {
+                                                           const float* __restrict__ partial, int nparts, int intz) {
   float lo = __builtin_inff(), hi = -__builtin_inff();
   for (int i = threadIdx.x; i < nparts; i += 256) {
     lo = __builtin_fminf(lo, partial[2 * i]);
     hi = __builtin_fmaxf(hi, partial[2 * i + 1]);
   }
   block_minmax(lo, hi);
-  const QParams p = qparams(lo, hi);
+  const QParams p = qparams(lo, hi, intz != 0);
   for (int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x; gw < total_words; gw += (int64_t)gridDim.x * 256) {
     float v[8];
     load8<DT>(W, gw * 8, v);
-    packed[gw] = (int32_t)pack8(v, p);
+    packed[gw] = (int32_t)pack8(v, p, intz != 0);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     scales[0] = p.sb;
@@ -260,22 +267,22 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
 
 template <int DT>
 static hipError_t quant_small_dispatch(int T, const void* W, int32_t* packed, uint16_t* scales, uint16_t* zeros,
-                                       int64_t total_words, hipStream_t st) {
+                                       int64_t total_words, int intz, hipStream_t st) {
   const dim3 grid((unsigned)((total_words + 255) / 256)), block(256);
   switch (T) {
-    case 2: quant_small_kernel<DT, 2><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
-    case 4: quant_small_kernel<DT, 4><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
-    case 8: quant_small_kernel<DT, 8><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
-    case 16: quant_small_kernel<DT, 16><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
-    case 32: quant_small_kernel<DT, 32><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
-    case 64: quant_small_kernel<DT, 64><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words); break;
+    case 2: quant_small_kernel<DT, 2><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 4: quant_small_kernel<DT, 4><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 8: quant_small_kernel<DT, 8><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 16: quant_small_kernel<DT, 16><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 32: quant_small_kernel<DT, 32><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 64: quant_small_kernel<DT, 64><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int DT>
-static hipError_t quantize_dt(const void* W, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+static hipError_t quantize_dt(const void* W, int64_t N, int64_t K, int mode, int g, int intz, int32_t* packed,
                               uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st) {
   const int64_t total_words = N * (K / 8);
   if (mode == W4_MODE_GLOBAL) {
@@ -287,24 +294,25 @@ static hipError_t quantize_dt(const void* W, int64_t N, int64_t K, int mode, int
     if (e != hipSuccess) return e;
     const int64_t qb = (total_words + 255) / 256;
     const int qgrid = (int)(qb < 8192 ? qb : 8192);
-    quant_global_kernel<DT><<<qgrid, 256, 0, st>>>(W, packed, scales, zeros, total_words, partial, nb);
+    quant_global_kernel<DT><<<qgrid, 256, 0, st>>>(W, packed, scales, zeros, total_words, partial, nb, intz);
     return hipGetLastError();
   }
   const int64_t gsize = mode == W4_MODE_ROWWISE ? K : g;
   const int64_t wpg = gsize / 8;
   if (wpg <= 64 && (wpg & (wpg - 1)) == 0 && wpg >= 2)
-    return quant_small_dispatch<DT>((int)wpg, W, packed, scales, zeros, total_words, st);
+    return quant_small_dispatch<DT>((int)wpg, W, packed, scales, zeros, total_words, intz, st);
   const int64_t ngroups = total_words / wpg;
-  quant_large_kernel<DT><<<(unsigned)((ngroups + 3) / 4), 256, 0, st>>>(W, packed, scales, zeros, ngroups, (int)wpg);
+  quant_large_kernel<DT><<<(unsigned)((ngroups + 3) / 4), 256, 0, st>>>(W, packed, scales, zeros, ngroups, (int)wpg,
+                                                                         intz);
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int32_t* packed,
+hipError_t launch_quantize(const void* W, int dt, int64_t N, int64_t K, int mode, int g, int intz, int32_t* packed,
                            uint16_t* scales, uint16_t* zeros, void* ws, hipStream_t st) {
   switch (dt) {
-    case W4_DT_F32: return quantize_dt<W4_DT_F32>(W, N, K, mode, g, packed, scales, zeros, ws, st);
-    case W4_DT_F16: return quantize_dt<W4_DT_F16>(W, N, K, mode, g, packed, scales, zeros, ws, st);
-    case W4_DT_BF16: return quantize_dt<W4_DT_BF16>(W, N, K, mode, g, packed, scales, zeros, ws, st);
+    case W4_DT_F32: return quantize_dt<W4_DT_F32>(W, N, K, mode, g, intz, packed, scales, zeros, ws, st);
+    case W4_DT_F16: return quantize_dt<W4_DT_F16>(W, N, K, mode, g, intz, packed, scales, zeros, ws, st);
+    case W4_DT_BF16: return quantize_dt<W4_DT_BF16>(W, N, K, mode, g, intz, packed, scales, zeros, ws, st);
   }
   return hipErrorInvalidValue;
 }

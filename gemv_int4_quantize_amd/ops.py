@@ -63,6 +63,22 @@ class QuantizedWeight:
     def desc(self) -> W4Desc:
         return W4Desc(self.N, self.K, self.mode, self.group if self.mode == MODE_GROUPWISE else 0)
 
+    def packed_bytes(self) -> torch.Tensor:
+        """The packed codes as INT8 words: uint8 [N][K/2], two codes per byte, low nibble
+        first -- the same bytes as the int32 words (a view, no copy)."""
+        return self.packed.view(torch.uint8)
+
+    @classmethod
+    def from_bytes(cls, packed_u8: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, mode, group=None):
+        """Wrap INT8-packed codes (uint8 [N][K/2], 4-byte aligned, contiguous) without a copy."""
+        if packed_u8.dtype != torch.uint8 or packed_u8.dim() != 2 or not packed_u8.is_contiguous():
+            raise ValueError("packed_u8 must be a contiguous uint8 [N][K/2] tensor")
+        if packed_u8.shape[1] % 4 or packed_u8.data_ptr() % 4:
+            raise ValueError("INT8-packed rows must hold a multiple of 8 codes and be 4-byte aligned")
+        N, K = packed_u8.shape[0], packed_u8.shape[1] * 2
+        m = mode_id(mode)
+        return cls(packed_u8.view(torch.int32), scales, zeros, N, K, m, int(group) if m == MODE_GROUPWISE else 0)
+
     def mm(self, x: torch.Tensor, bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
         """Y = X @ w^T (+ bias)."""
         return mm(x, self, transposed=False, bias=bias, out=out)
@@ -92,11 +108,15 @@ def empty_quantized(N: int, K: int, mode, group: int | None, device) -> Quantize
         N=N, K=K, mode=m, group=g)
 
 
-def quantize_pack_into(W: torch.Tensor, qw: QuantizedWeight, row0: int = 0) -> None:
+_ZERO = {"fp16": _lib.ZERO_FP16, "int": _lib.ZERO_INT}
+
+
+def quantize_pack_into(W: torch.Tensor, qw: QuantizedWeight, row0: int = 0, zero: str = "fp16") -> None:
     """Quantize W [n][K] into rows row0 .. row0+n of an existing packed weight.
 
     Used to fuse projections (for example Q, K and V) into one packed operand
     without a copy: each part is quantized straight into its row slice.
+    zero="int" rounds each zero point to an integer in [0, 15] (AWQ style).
     """
     _need_cuda(W, qw.packed)
     if W.dim() != 2 or not W.is_contiguous():
@@ -120,19 +140,20 @@ def quantize_pack_into(W: torch.Tensor, qw: QuantizedWeight, row0: int = 0) -> N
     scales = qw.scales[mrow:mrow + (1 if qw.mode == MODE_GLOBAL else n)]
     zeros = qw.zeros[mrow:mrow + (1 if qw.mode == MODE_GLOBAL else n)]
     assert scales.shape[1] == gpr
-    check(L.w4_quantize_pack(_ptr(W), dt, ctypes.byref(desc), _ptr(packed), _ptr(scales), _ptr(zeros),
-                             _ptr(ws), ws_bytes.value, _stream(W.device)))
+    check(L.w4_quantize_pack_zp(_ptr(W), dt, ctypes.byref(desc), _ZERO[zero], _ptr(packed), _ptr(scales),
+                                _ptr(zeros), _ptr(ws), ws_bytes.value, _stream(W.device)))
 
 
-def quantize_pack(W: torch.Tensor, mode="groupwise", group: int | None = 128) -> QuantizedWeight:
-    """Quantize and pack W [N][K] (fp32, fp16 or bf16) to asymmetric uint4."""
+def quantize_pack(W: torch.Tensor, mode="groupwise", group: int | None = 128, zero: str = "fp16") -> QuantizedWeight:
+    """Quantize and pack W [N][K] (fp32, fp16 or bf16) to asymmetric uint4; zero="int" gives
+    integer zero points (AWQ style)."""
     N, K = W.shape
     qw = empty_quantized(N, K, mode, group, W.device)
-    quantize_pack_into(W, qw, 0)
+    quantize_pack_into(W, qw, 0, zero)
     return qw
 
 
-def quantize_fused(parts, mode="groupwise", group: int | None = 128) -> QuantizedWeight:
+def quantize_fused(parts, mode="groupwise", group: int | None = 128, zero: str = "fp16") -> QuantizedWeight:
     """Quantize several [n_i][K] weights into one row-concatenated packed operand (fused QKV)."""
     K = parts[0].shape[1]
     N = sum(p.shape[0] for p in parts)
@@ -141,7 +162,7 @@ def quantize_fused(parts, mode="groupwise", group: int | None = 128) -> Quantize
     qw = empty_quantized(N, K, mode, group, parts[0].device)
     r = 0
     for p in parts:
-        quantize_pack_into(p, qw, r)
+        quantize_pack_into(p, qw, r, zero)
         r += p.shape[0]
     return qw
 

@@ -63,6 +63,10 @@ typedef enum { W4_DT_F32 = 0, W4_DT_F16 = 1, W4_DT_BF16 = 2 } w4_dtype;
 
 typedef enum { W4_OP_QUANTIZE = 0, W4_OP_MM = 1, W4_OP_MM_T = 2, W4_OP_DEQUANTIZE = 3 } w4_op;
 
+/* Zero-point kind of a quantization: a real fp16 zero (the default), or an
+ * integer zero point in [0, 15] (AWQ style), also stored in the fp16 zeros. */
+typedef enum { W4_ZERO_FP16 = 0, W4_ZERO_INT = 1 } w4_zero_kind;
+
 /* Shape and grouping of one quantized weight.  N >= 1 rows, K >= 8 columns,
  * K % 8 == 0.  `group` is the GROUPWISE group size g along K (a power of two in
  * [16, 4096] with K % g == 0); it is ignored for GLOBAL and ROWWISE. */
@@ -94,6 +98,19 @@ int w4_workspace_bytes(const w4_desc* desc, int op, int64_t M, size_t* bytes);
 int w4_quantize_pack(const void* W, int w_dtype, const w4_desc* desc,
                      int32_t* packed, uint16_t* scales, uint16_t* zeros,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* w4_quantize_pack with a choice of zero point.  W4_ZERO_FP16 is
+ * w4_quantize_pack.  W4_ZERO_INT rounds the zero point to an integer, the AWQ
+ * style of the W4A16 AWQ g = 128 workload of "Modify small-batched weight only
+ * quantization":  z = clamp(rint((0 - min) / s), 0, 15),
+ * q = clamp(rint(w / s) + z, 0, 15)  (s as above), so q - z is an integer and
+ * the weight operand is bf16_rne((q - z) * s).  The zero is stored in the same
+ * fp16 zeros array (exactly), so every other entry point reads either kind.
+ * zero_kind outside these two is W4_ERR_INVALID; the rest is as for
+ * w4_quantize_pack. */
+int w4_quantize_pack_zp(const void* W, int w_dtype, const w4_desc* desc, int zero_kind,
+                        int32_t* packed, uint16_t* scales, uint16_t* zeros,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Dequantize packed weights to out [N][K]: out_dtype W4_DT_BF16 writes the
  * matmul operand bf16_rne(fp32(q - z) * s), W4_DT_F32 writes fp32(q - z) * s.

@@ -41,6 +41,11 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   a hand-derived golden row (tests/golden/quant_row.txt), invariants
   (code range, min->0 / max->15, error bound, ROWWISE == GROUPWISE(g=K)).
 * pack / unpack: the golden word of the LSB-first layout, bijection both ways.
+* pack_bytes (INT8 packing): golden bytes of the same codes; the int32 words
+  viewed as little-endian bytes equal it.
+* quantize with integer zero points: the same exact-rational brute force in
+  AWQ's order (round, then add the integer zero), and invariants (integer zero
+  in [0, 15], exact zero maps to code z and dequantizes to exactly 0).
 * dequantize: all 16 codes against an exact-rational bf16 rounding.
 * matmul: exact-rational triple loop on tiny shapes, one-hot pins of the layout
   in both modes, constant-code closed form, linearity and bias.
@@ -58,7 +63,7 @@ import numpy as np
 
 __all__ = [
     "GLOBAL", "ROWWISE", "GROUPWISE", "MODE_NAMES",
-    "meta_shape", "to_f32", "quantize", "pack", "unpack", "quantize_pack",
+    "meta_shape", "to_f32", "quantize", "pack", "unpack", "quantize_pack", "pack_bytes",
     "dequantize_f32", "bf16_rne_bits", "bf16_bits_to_f64", "dequantize_bf16_bits",
     "matmul", "round_output", "fuse_rows", "mae", "compression_ratio", "page_compression_ratio",
 ]
@@ -107,12 +112,18 @@ def _grouped(w32: np.ndarray, mode: int, g: int | None) -> np.ndarray:
     return w32.reshape(N, K // g, g)
 
 
-def quantize(w32: np.ndarray, mode: int, g: int | None = None):
+def quantize(w32: np.ndarray, mode: int, g: int | None = None, int_zero: bool = False):
     """Asymmetric uint4 codes with an fp16 scale and zero per group.
 
     Follows Objective 1 of "Quantized LLM Inference with Triton Kernels"
     (FP16 -> INT4, global / rowwise / groupwise) with readings 1 and 2 of the
     module docstring.  Returns ``(q uint8 [N][K], scales fp16, zeros fp16)``.
+
+    ``int_zero``: the integer zero point of the AWQ format named by "Modify
+    small-batched weight only quantization" (W4A16 AWQ, g = 128), in AWQ's order:
+    ``z = clamp(rint((0 - min) / s), 0, 15)`` and ``q = clamp(rint(w / s) + z, 0, 15)``
+    (rounding before the integer add; the two orders differ at ties).  The zero is
+    stored as the fp16 value of that integer.
     """
     w32 = np.asarray(w32, dtype=_F32)
     N, K = w32.shape
@@ -126,11 +137,16 @@ def quantize(w32: np.ndarray, mode: int, g: int | None = None):
         s16 = np.where((s16 == 0) | ~np.isfinite(s16), _F16(1.0), s16)
         s_f = s16.astype(_F32)
         z32 = (_F32(0.0) - lo) / s_f               # 0 - lo keeps an all-zero group's zero at +0
-        z16 = z32.astype(_F16)
-        z_f = z16.astype(_F32)
-        t = grp / s_f[..., None] + z_f[..., None]  # two fp32 ops, each rounded
+        if int_zero:
+            z_f = np.clip(np.rint(z32), 0, 15).astype(_F32)   # an integer in [0, 15]
+            z16 = z_f.astype(_F16)                             # exact
+            t = np.rint(grp / s_f[..., None]) + z_f[..., None]  # round, then the exact integer add
+        else:
+            z16 = z32.astype(_F16)
+            z_f = z16.astype(_F32)
+            t = grp / s_f[..., None] + z_f[..., None]  # two fp32 ops, each rounded
     assert not np.any(np.isnan(t)), "code argument is NaN (zero overflowed fp16)"
-    q = np.clip(np.rint(t), 0, 15).astype(np.uint8)  # rint: round half to even
+    q = np.clip(np.rint(t), 0, 15).astype(np.uint8)  # rint: round half to even (a no-op for int_zero)
     return q.reshape(N, K), s16.reshape(meta_shape(N, K, mode, g)), z16.reshape(meta_shape(N, K, mode, g))
 
 
@@ -160,10 +176,20 @@ def unpack(packed: np.ndarray) -> np.ndarray:
     return q.reshape(N, C * 8)
 
 
-def quantize_pack(w32: np.ndarray, mode: int, g: int | None = None):
+def quantize_pack(w32: np.ndarray, mode: int, g: int | None = None, int_zero: bool = False):
     """Quantize then pack: returns ``(packed int32 [N][K/8], scales fp16, zeros fp16)``."""
-    q, s, z = quantize(w32, mode, g)
+    q, s, z = quantize(w32, mode, g, int_zero)
     return pack(q), s, z
+
+
+def pack_bytes(q: np.ndarray) -> np.ndarray:
+    """INT8 packing of Objective 1 of "Quantized LLM Inference with Triton Kernels":
+    two codes per byte, code ``k = 2b + j`` in bits 4j..4j+3 of byte b (uint8 [N][K/2])."""
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    assert K % 2 == 0
+    q2 = q.reshape(N, K // 2, 2)
+    return ((q2[:, :, 0] & 0xF) | ((q2[:, :, 1] & 0xF) << 4)).astype(np.uint8)
 
 
 def _expand_meta(meta: np.ndarray, N: int, K: int) -> np.ndarray:

@@ -74,6 +74,15 @@ def rint_clamp_0_15(t: Fraction) -> int:
     return best[1]
 
 
+def rint_half_even(t: Fraction) -> int:
+    """The nearest integer to t, ties to the even one (no clamping)."""
+    f = t.numerator // t.denominator  # floor
+    rem = t - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        return f + 1
+    return f
+
+
 def bf16_from_fraction_bits(v) -> int:
     """uint16 bit pattern of a bf16 value given exactly (Fraction or +/-inf)."""
     if isinstance(v, float) and math.isinf(v):

@@ -122,6 +122,10 @@ def test_quantize_validation_before_launch():
     dg = _lib.W4Desc(64, 128, _lib.MODE_GLOBAL, 0)
     assert q(a16, 1, ctypes.byref(dg), a16, a16, a16, None, 0, None) == _lib.W4_ERR_RESOURCE
     assert q(a16, 1, ctypes.byref(dg), a16, a16, a16, a16, 16, None) == _lib.W4_ERR_RESOURCE
+    qz = L.w4_quantize_pack_zp
+    assert qz(a16, 1, ctypes.byref(d), 7, a16, a16, a16, None, 0, None) == _lib.W4_ERR_INVALID
+    assert qz(a16, 1, ctypes.byref(d), _lib.ZERO_INT, ctypes.c_void_p(0x10002), a16, a16, None, 0, None) == \
+        _lib.W4_ERR_ALIGN
     dq = L.w4_dequantize
     assert dq(a16, a16, a16, ctypes.byref(d), a16, _lib.DT_F16, None) == _lib.W4_ERR_INVALID
     assert dq(a16, a16, a16, ctypes.byref(d), ctypes.c_void_p(0x10004), _lib.DT_BF16, None) == _lib.W4_ERR_ALIGN

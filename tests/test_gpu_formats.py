@@ -1,0 +1,85 @@
+"""GPU parity of the format variants: integer zero points (AWQ style) and INT8-word packing."""
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_int4_quantize_amd as w4
+import oracle as O
+import synth
+from gpu_helpers import DEV, assert_mm_close, assert_quant_equal, dev_bf16, dev_f32, dev_weight, host
+
+pytestmark = pytest.mark.gpu
+
+OMODE = {"global": O.GLOBAL, "rowwise": O.ROWWISE, "groupwise": O.GROUPWISE}
+MODES = [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 64), ("groupwise", 128),
+         ("groupwise", 1024)]
+
+
+def _special_weight(N, K, seed):
+    r = np.random.default_rng(seed)
+    w = (r.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[0, :] = 0.0                       # all-zero row
+    w[1, : K // 2] = 0.75               # constant half row
+    w[2, :] = np.abs(w[2, :]) + 0.1     # all positive: the zero point clamps at 0
+    w[3, :] = -np.abs(w[3, :]) - 0.1    # all negative: the zero point clamps at 15
+    w[4, 5] = 3.0                       # outliers
+    w[5, 17] = -2.5
+    w[6, ::7] = 0.0                     # exact zeros inside a normal row
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode,g", MODES, ids=[f"{m}{g or ''}" for m, g in MODES])
+def test_int_zero_quantize_bit_exact(dtype, mode, g):
+    print(f"[case] int-zero quantize dtype={dtype} mode={mode} g={g}", flush=True)
+    N, K = 37, 4096
+    w = synth.weight(730, 0, N, K, dtype) if dtype != "f32" else _special_weight(N, K, 730)
+    w32 = O.to_f32(w, dtype)
+    ref = O.quantize_pack(w32, OMODE[mode], g, int_zero=True)
+    qw = w4.quantize_pack(dev_weight(w, dtype), mode, g, zero="int")
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"int zero {dtype} {mode}{g}")
+    z = host(qw.zeros.float())
+    assert np.all(z == np.round(z)) and z.min() >= 0 and z.max() <= 15
+
+
+@pytest.mark.parametrize("M,tr", [(1, False), (4, False), (200, False), (200, True)])
+@pytest.mark.parametrize("mode,g", [("rowwise", None), ("groupwise", 128)], ids=["rowwise", "g128"])
+def test_int_zero_matmul(M, tr, mode, g):
+    """Integer zero points need no matmul change: parity on the GEMV, GEMM and transposed paths."""
+    N, K = 520, 2048
+    print(f"[case] int-zero matmul M={M} t={tr} {mode}{g or ''}", flush=True)
+    w = synth.weight(731, M, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g, int_zero=True)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g, zero="int")
+    a = synth.activations_bf16(731, M, M, N if tr else K)
+    bias = synth.bias_f32(731, M, K if tr else N)
+    y = w4.mm(dev_bf16(a), qw, transposed=tr, bias=dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(a, *ref, K, tr, bias=bias), f"int zero M={M} t={tr} {mode}{g}")
+
+
+def test_int_zero_fused_qkv():
+    K = 1024
+    sizes = (256, 128, 128)
+    ws = [synth.weight(732, i, n, K, "bf16", tensor_id=synth.T_Q + i) for i, n in enumerate(sizes)]
+    fused = w4.quantize_fused([dev_weight(w, "bf16") for w in ws], "groupwise", 128, zero="int")
+    refs = [O.quantize_pack(O.to_f32(w, "bf16"), O.GROUPWISE, 128, int_zero=True) for w in ws]
+    assert_quant_equal(fused, *O.fuse_rows(refs), what="fused int zero")
+
+
+def test_int8_word_view_and_wrap():
+    """INT8 packing: the packed weight viewed as bytes equals the oracle's two-codes-per-byte
+    packing, and a weight wrapped from such bytes (uploaded from the oracle) multiplies to
+    the oracle's product."""
+    N, K, M = 136, 1024, 3
+    w = synth.weight(733, 0, N, K, "f16")
+    w32 = O.to_f32(w, "f16")
+    q, s, z = O.quantize(w32, O.GROUPWISE, 64)
+    qw = w4.quantize_pack(dev_weight(w, "f16"), "groupwise", 64)
+    np.testing.assert_array_equal(host(qw.packed_bytes()), O.pack_bytes(q))
+    u8 = torch.from_numpy(O.pack_bytes(q)).to(DEV)
+    wrapped = w4.QuantizedWeight.from_bytes(u8, torch.from_numpy(s).to(DEV), torch.from_numpy(z).to(DEV),
+                                            "groupwise", 64)
+    x = synth.activations_bf16(733, 0, M, K)
+    assert_mm_close(host(w4.mm(dev_bf16(x), wrapped)), O.matmul(x, O.pack(q), s, z, K), "int8-wrapped weight")

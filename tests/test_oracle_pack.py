@@ -86,3 +86,13 @@ def test_meta_expansion_per_mode():
                 else:
                     want = n * (K // 16) + k // 16 + 1.0
                 assert deq[n, k] == want
+
+
+def test_pack_bytes_golden_and_word_view():
+    """INT8 packing: two codes per byte, low nibble first (written out by hand), and the
+    int32 words of the INT32 packing viewed as little-endian bytes are the same bytes."""
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 15, 0, 0, 15, 9, 10, 11, 12]], dtype=np.uint8)
+    want = np.array([[0x21, 0x43, 0x65, 0x87, 0x0F, 0xF0, 0xA9, 0xCB]], dtype=np.uint8)
+    np.testing.assert_array_equal(O.pack_bytes(q), want)
+    r = np.random.default_rng(5).integers(0, 16, size=(7, 64), dtype=np.uint8)
+    np.testing.assert_array_equal(O.pack(r).view(np.uint8).reshape(7, 32), O.pack_bytes(r))

@@ -166,3 +166,68 @@ def test_bf16_input_is_exact():
     b = synth.weight(99, 2, 8, 64, "bf16")
     w32 = O.to_f32(b, "bf16")
     assert np.array_equal(synth.f32_to_bf16_bits(w32), b)
+
+
+def _brute_quantize_int_zero(w32, mode, g):
+    """Exact-rational brute force of the integer-zero (AWQ order) quantizer."""
+    from exact import rint_half_even
+    N, K = w32.shape
+    if mode == O.GLOBAL:
+        groups = [[(n, k) for n in range(N) for k in range(K)]]
+    elif mode == O.ROWWISE:
+        groups = [[(n, k) for k in range(K)] for n in range(N)]
+    else:
+        groups = [[(n, k) for k in range(c * g, (c + 1) * g)] for n in range(N) for c in range(K // g)]
+    q = np.zeros((N, K), dtype=np.uint8)
+    ss, zz = [], []
+    for grp in groups:
+        vals = [frac(w32[n, k]) for n, k in grp]
+        lo, hi = min(vals), max(vals)
+        s16 = round_fmt(round_fmt(round_fmt(hi - lo, "f32") / 15, "f32"), "f16")
+        if s16 == 0 or isinstance(s16, float):
+            s16 = 1
+        z = min(max(rint_half_even(round_fmt((0 - lo) / s16, "f32")), 0), 15)
+        for (n, k), v in zip(grp, vals):
+            q[n, k] = min(max(rint_half_even(round_fmt(v / s16, "f32")) + z, 0), 15)
+        ss.append(float(s16))
+        zz.append(float(z))
+    shp = O.meta_shape(N, K, mode, g)
+    return q, np.array(ss).reshape(shp), np.array(zz).reshape(shp)
+
+
+@pytest.mark.parametrize("name,w", _tiny_inputs(), ids=[c[0] for c in _tiny_inputs()])
+def test_bruteforce_int_zero(name, w):
+    K = w.shape[1]
+    for mode, g in [(O.GLOBAL, None), (O.ROWWISE, None), (O.GROUPWISE, 16), (O.GROUPWISE, 32), (O.GROUPWISE, K)]:
+        q, s, z = O.quantize(w, mode, g, int_zero=True)
+        qb, sb, zb = _brute_quantize_int_zero(w, mode, g)
+        assert np.array_equal(s.astype(np.float64), sb), (name, mode, g)
+        assert np.array_equal(z.astype(np.float64), zb), (name, mode, g)
+        assert np.array_equal(q, qb), (name, mode, g)
+
+
+def test_int_zero_order_matters_at_ties():
+    """Rounding w/s before adding the integer zero (AWQ's order) differs from rounding
+    w/s + z when w/s is a half-integer and z is odd: pin one such element."""
+    # group [-1.5, ..., 6.0]: s = fp16(7.5 / 15) = 0.5, z = rint(1.5 / 0.5) = 3 (odd);
+    # w = 0.25 -> w / s = 0.5 -> rint = 0 -> q = 3, whereas rint(0.5 + 3) = 4
+    w = np.array([[-1.5, 6.0, 0.25, 0.0] + [0.0] * 12], dtype=np.float32)
+    q, s, z = O.quantize(w, O.GROUPWISE, 16, int_zero=True)
+    assert float(s[0, 0]) == 0.5 and float(z[0, 0]) == 3.0
+    assert q[0, 2] == 3 and q[0, 3] == 3 and q[0, 0] == 0 and q[0, 1] == 15
+
+
+@pytest.mark.parametrize("mode,g", [(O.ROWWISE, None), (O.GROUPWISE, 32), (O.GROUPWISE, 128)])
+def test_int_zero_invariants(mode, g):
+    w = synth.weight(11, 0, 48, 256, "f32")
+    w[3, :40] = 0.0
+    q, s, z = O.quantize(w, mode, g, int_zero=True)
+    zf = z.astype(np.float64)
+    assert np.all(zf == np.round(zf)) and zf.min() >= 0 and zf.max() <= 15
+    # an exact zero weight (with min <= 0 <= max in its group) gets code z and dequantizes to 0
+    deq = O.dequantize_f32(O.pack(q), s, z, w.shape[1])
+    zero_pos = w == 0.0
+    assert np.all(deq[zero_pos] == 0.0)
+    # every in-range weight is within half a step of its dequantized value (up to rounding)
+    sx = _expand(s, *w.shape)
+    assert np.all(np.abs(deq - w) <= 0.5 * sx * (1 + 1e-3) + 1e-7)
