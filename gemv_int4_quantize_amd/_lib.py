@@ -67,7 +67,8 @@ def lib() -> ctypes.CDLL:
     L.w4_quantize_pack_zp.argtypes = [vp, i32, pdesc, i32, vp, vp, vp, vp, sz, vp]
     L.w4_dequantize.argtypes = [vp, vp, vp, pdesc, vp, i32, vp]
     L.w4a16_mm.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp, sz, vp]
-    L.w4a16_mm_out.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz, vp]
+    L.w4a16_mm_out.argtypes = [vp, i32, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz,
+                               vp]
     L.w4a16_mm_kernel.argtypes = [i64, pdesc, i32]
     L.w4a16_mm_kernel.restype = ctypes.c_char_p
     L.w4_status_string.argtypes = [i32]

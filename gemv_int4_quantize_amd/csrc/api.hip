@@ -144,8 +144,10 @@ int make_epi(const w4_desc* desc, int transposed, int64_t M, const void* bias, i
 }
 
 w4::MmArgs make_args(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
-                     const uint16_t* zeros, const w4_desc* desc, int transposed, const w4::Epi& ep) {
+                     const uint16_t* zeros, const w4_desc* desc, int transposed, const w4::Epi& ep,
+                     bool a_f16 = false) {
   w4::MmArgs a;
+  a.a_f16 = a_f16;
   a.A = A;
   a.packed = packed;
   a.scales = scales;
@@ -238,8 +240,8 @@ int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t*
                   void* out, int out_dtype, void* stream) {
   int s = check_desc(desc);
   if (s != W4_OK) return s;
-  if (out_dtype != W4_DT_BF16 && out_dtype != W4_DT_F32)
-    return fail(W4_ERR_INVALID, "out_dtype = %d must be BF16 or F32", out_dtype);
+  if (out_dtype != W4_DT_BF16 && out_dtype != W4_DT_F32 && out_dtype != W4_DT_F16)
+    return fail(W4_ERR_INVALID, "out_dtype = %d must be BF16, F16 or F32", out_dtype);
   if (!packed || !scales || !zeros || !out) return fail(W4_ERR_INVALID, "a required pointer is NULL");
   if (!aligned(out, 16) || !aligned(packed, 4) || !aligned(scales, 2) || !aligned(zeros, 2))
     return fail(W4_ERR_ALIGN, "out must be 16-byte, packed 4-byte, scales / zeros 2-byte aligned");
@@ -264,16 +266,20 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
   return run_mm(make_args(A, M, packed, scales, zeros, desc, transposed, ep), ws, ws_bytes, stream);
 }
 
-int w4a16_mm_out(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
-                 const w4_desc* desc, int transposed, const void* bias, int out_dtype, const w4_out_seg* segs,
-                 int nsegs, void* ws, size_t ws_bytes, void* stream) {
-  int s = check_mm(A, M, packed, scales, zeros, desc, transposed);
+int w4a16_mm_out(const void* A, int a_dtype, int64_t M, const int32_t* packed, const uint16_t* scales,
+                 const uint16_t* zeros, const w4_desc* desc, int transposed, const void* bias, int out_dtype,
+                 const w4_out_seg* segs, int nsegs, void* ws, size_t ws_bytes, void* stream) {
+  if (a_dtype != W4_DT_BF16 && a_dtype != W4_DT_F16)
+    return fail(W4_ERR_INVALID, "a_dtype = %d must be BF16 or F16", a_dtype);
+  const uint16_t* A16 = static_cast<const uint16_t*>(A);
+  int s = check_mm(A16, M, packed, scales, zeros, desc, transposed);
   if (s != W4_OK) return s;
   w4::Epi ep;
   s = make_epi(desc, transposed, M, bias, out_dtype, segs, nsegs, &ep);
   if (s != W4_OK) return s;
   if (M == 0) return ok();
-  return run_mm(make_args(A, M, packed, scales, zeros, desc, transposed, ep), ws, ws_bytes, stream);
+  return run_mm(make_args(A16, M, packed, scales, zeros, desc, transposed, ep, a_dtype == W4_DT_F16), ws, ws_bytes,
+                stream);
 }
 
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {

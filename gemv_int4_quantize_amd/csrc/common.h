@@ -124,11 +124,76 @@ __device__ __forceinline__ void dq_word_f32(uint32_t w, const DqConst& c, float 
   v[7] = fma_mix_hi(e, c.s20, c.nzs);
 }
 
+// Two fp32 values -> one dword holding fp16_rne(lo) | fp16_rne(hi) << 16 (v_cvt_pk_f16_f32:
+// src0 to the low half, round to nearest even; checked on gfx950 against per-value
+// conversion over ties, subnormals and overflow).
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  uint32_t d;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(d) : "v"(lo), "v"(hi));
+  return d;
+}
+
+// One packed word -> 4 dwords of fp16 pairs in K order, each fp16_rne(fp32((q - z) * s)):
+// the fp32 values of dq_word_bf16, rounded to fp16.  17 VALU instructions.
+__device__ __forceinline__ void dq_word_f16(uint32_t w, const DqConst& c, uint32_t out[4]) {
+  float v[8];
+  dq_word_f32(w, c, v);
+  out[0] = pack_f16x2(v[0], v[1]);
+  out[1] = pack_f16x2(v[2], v[3]);
+  out[2] = pack_f16x2(v[4], v[5]);
+  out[3] = pack_f16x2(v[6], v[7]);
+}
+
+// Weight operand of one packed word in the activation dtype (bf16 or fp16 pairs).
+template <bool F16>
+__device__ __forceinline__ void dq_word_op(uint32_t w, const DqConst& c, uint32_t out[4]) {
+  if constexpr (F16) dq_word_f16(w, c, out);
+  else dq_word_bf16(w, c, out);
+}
+
+// Two words of consecutive rows (contraction index) -> 8 operand pairs, pair j holding column
+// j of both rows (the transposed operand layout).
+template <bool F16>
+__device__ __forceinline__ void dq_rows_op(uint32_t w0, const DqConst& c0, uint32_t w1, const DqConst& c1,
+                                           uint32_t out[8]) {
+  float v0[8], v1[8];
+  dq_word_f32(w0, c0, v0);
+  dq_word_f32(w1, c1, v1);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = F16 ? pack_f16x2(v0[j], v1[j]) : pack_bf16x2(v0[j], v1[j]);
+}
+
+// acc += a.lo * b.lo + a.hi * b.hi on fp16 pairs, fp32 accumulate (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
+
 // acc += a.lo * b.lo + a.hi * b.hi on bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc,
                                          false);
+}
+
+template <bool F16>
+__device__ __forceinline__ float dot2_op(uint32_t a, uint32_t b, float acc) {
+  if constexpr (F16) return dot2_f16(a, b, acc);
+  else return dot2_bf16(a, b, acc);
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// One 32x32x16 MFMA on operand bits (eight bf16 or fp16 values per lane), fp32 accumulate.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma_op(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                  0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
 }
 
 // Meta-data addressing: one (scale, zero) per row-group.

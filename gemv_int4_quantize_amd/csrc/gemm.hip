@@ -42,7 +42,6 @@
 
 namespace w4 {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // raw buffer resource (gfx9-class dword 3: 32-bit data format); loads past `bytes` read 0
@@ -59,7 +58,8 @@ constexpr int lds_row() { return BK + 8; }
 // one group covers all of its words (rowwise, global, or g >= its span), else one per word.
 // STAGES: 2 (loads of step k+1 in flight during step k), 3 (loads of step k+2), or 4 (two LDS
 // stages, loads of step k+2, stores of step k+1 interleaved with the MFMAs of step k).
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES>
+// F16: fp16 activations and weight operand (v_mfma_f32_32x32x16_f16), else bf16.
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES, bool F16>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A,
                                                             const int32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
@@ -277,7 +277,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < W_PER_T; ++i) {
         uint32_t o[4];
-        dq_word_bf16(R.w[i], MPT == 1 ? d0 : dq_const_mix(R.s[i], R.z[i]), o);
+        dq_word_op<F16>(R.w[i], MPT == 1 ? d0 : dq_const_mix(R.s[i], R.z[i]), o);
         *reinterpret_cast<u32x4*>(bs + row * LR + (w0 + i) * 8) = u32x4{o[0], o[1], o[2], o[3]};
       }
     } else {
@@ -286,21 +286,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       constexpr int WCOLS = BN / 8;
       const int wc = tid % WCOLS;
       const int rb = tid / WCOLS;
-      float v[W_PER_T][8];
+      // pk[p][j]: column j of rows 2p, 2p + 1 as one operand pair
+      constexpr int NP = (W_PER_T + 1) / 2;
+      uint32_t pk[NP][8];
 #pragma unroll
-      for (int i = 0; i < W_PER_T; ++i) dq_word_f32(R.w[i], dq_const_mix(R.s[i], R.z[i]), v[i]);
+      for (int p = 0; p < NP; ++p) {
+        const int i1 = 2 * p + 1 < W_PER_T ? 2 * p + 1 : 2 * p;
+        dq_rows_op<F16>(R.w[2 * p], dq_const_mix(R.s[2 * p], R.z[2 * p]), R.w[i1], dq_const_mix(R.s[i1], R.z[i1]),
+                        pk[p]);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         uint16_t* dst = bs + (wc * 8 + j) * LR + bswz(wc * 8 + j, rb * W_PER_T);
         if constexpr (W_PER_T == 8) {
-          *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j]),
-                                                 pack_bf16x2(v[4][j], v[5][j]), pack_bf16x2(v[6][j], v[7][j])};
+          *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0][j], pk[1][j], pk[2][j], pk[3][j]};
         } else if constexpr (W_PER_T == 4) {
-          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v[0][j], v[1][j]), pack_bf16x2(v[2][j], v[3][j])};
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0][j], pk[1][j]};
         } else if constexpr (W_PER_T == 2) {
-          *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(v[0][j], v[1][j]);
+          *reinterpret_cast<uint32_t*>(dst) = pk[0][j];
         } else {
-          *dst = (uint16_t)(pack_bf16x2(v[0][j], 0.0f) & 0xFFFFu);
+          *dst = (uint16_t)(pk[0][j] & 0xFFFFu);
         }
       }
     }
@@ -323,17 +328,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+      u32x4 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LR + kk * 16);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * LR + kk * 16);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
+        bfr[j] = *reinterpret_cast<const u32x4*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_op<F16>(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -357,17 +361,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     uint32_t pk[W_PER_T / 2][8];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+      u32x4 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * LR + kk * 16);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * LR + kk * 16);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
+        bfr[j] = *reinterpret_cast<const u32x4*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_op<F16>(af[i], bfr[j], acc[i][j]);
       // slice kk of the next step's stores
 #pragma unroll
       for (int q = 0; q < AU_PER; ++q) {
@@ -382,13 +385,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int pp = 0; pp < W_PER_T / 2; ++pp) {
         const int i = 2 * pp;  // rows i, i + 1 of the word column, in slice pp * KK / pairs
-        if (pp * KK / (W_PER_T / 2) == kk) {
-          float v0[8], v1[8];
-          dq_word_f32(R.w[i], dq_const_mix(R.s[i], R.z[i]), v0);
-          dq_word_f32(R.w[i + 1], dq_const_mix(R.s[i + 1], R.z[i + 1]), v1);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pk[i / 2][j] = pack_bf16x2(v0[j], v1[j]);
-        }
+        if (pp * KK / (W_PER_T / 2) == kk)
+          dq_rows_op<F16>(R.w[i], dq_const_mix(R.s[i], R.z[i]), R.w[i + 1], dq_const_mix(R.s[i + 1], R.z[i + 1]),
+                          pk[i / 2]);
       }
     }
 #pragma unroll
@@ -621,14 +620,14 @@ size_t lds_bytes(const Cfg& c) {
   return (size_t)(c.stages == 4 ? 2 : c.stages) * (c.wm * c.fm * 32 + c.wn * c.fn * 32) * (c.bk + 8) * 2;
 }
 
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
-hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META, bool F16>
+hipError_t run_k(const MmArgs& a, int splits, float* part, hipStream_t st) {
   constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
   // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
   const bool one = TRANS || META != META_GROUP || a.group >= 8 * WPT;
-  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES>
-               : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES>;
+  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES, F16>
+               : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES, F16>;
   const size_t lds = (size_t)(STAGES == 4 ? 2 : STAGES) * (BM + BN) * (BK + 8) * 2;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -647,6 +646,12 @@ hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, a.M, outc, a.ep, st);
+}
+
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
+hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
+  return a.a_f16 ? run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, true>(a, splits, part, st)
+                 : run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, false>(a, splits, part, st);
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>

@@ -1,6 +1,7 @@
 // Non-transposed MFMA W4A16 GEMM for gfx950 with the weight operand dequantized straight
 // into MFMA registers:  Y[m][n] = sum_k X[m][k] * w[n][k] (+ bias[n]),
-// w = bf16_rne((q - z) * s), bf16 MFMA operands, fp32 accumulation.
+// w = bf16_rne((q - z) * s), bf16 MFMA operands, fp32 accumulation (or, with fp16
+// activations, an fp16 weight operand and v_mfma_f32_32x32x16_f16).
 // Sources: Objective 2 of "Quantized LLM Inference with Triton Kernels" (Y = X_bf16 @
 // W_int4^T); "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560).
 //
@@ -36,7 +37,6 @@ namespace w4 {
 namespace {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 constexpr int kRsrcDword3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 class)
 
@@ -52,7 +52,7 @@ constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
 // (2 when g = 16).  KTAIL: K % 64 != 0 (activation columns past K are zeroed in LDS).
 // WB (META 1): bytes of one wide load = 2 max(1, 128 / g), a compile-time width so that the
 // loop holds exactly one load form.
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16>
 __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -175,21 +175,21 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto dequant = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], int kk, bf16x8 (&bfr)[FN]) {
+  auto dequant = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], int kk, u32x4 (&bfr)[FN]) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       uint32_t o[4];
-      dq_word_bf16(B.w[j][kk], dc[j][GPW == 2 ? kk / 2 : 0], o);
-      bfr[j] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+      dq_word_op<F16>(B.w[j][kk], dc[j][GPW == 2 ? kk / 2 : 0], o);
+      bfr[j] = u32x4{o[0], o[1], o[2], o[3]};
     }
   };
-  auto read_a = [&](const uint16_t* buf, int kk, bf16x8 (&af)[FM]) {
+  auto read_a = [&](const uint16_t* buf, int kk, u32x4 (&af)[FM]) {
     const uint16_t* as = buf + lr * kLR + h * 32 + kk * 8;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * kLR);
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * kLR);
   };
   auto compute = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], const uint16_t* buf) {
-    bf16x8 af[2][FM], bfr[2][FN];
+    u32x4 af[2][FM], bfr[2][FN];
     read_a(buf, 0, af[0]);
     dequant(B, dc, 0, bfr[0]);
 #pragma unroll
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bfr[c][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = mfma_op<F16>(af[c][i], bfr[c][j], acc[i][j]);
     }
   };
   // dequantization constants of step p (0: kt, 1: kt + 1) from the wide meta registers:
@@ -302,9 +302,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 }
 
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB = 0>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16>
 hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB>;
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16>;
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   const int lds = 2 * BM * kLR * 2;
   if (lds > 64 * 1024) {
@@ -325,24 +325,29 @@ hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) 
   return launch_splitk_reduce(part, splits, a.M, a.N, a.ep, st);
 }
 
-template <int FM, int FN, bool KTAIL>
+template <int FM, int FN, bool KTAIL, bool F16>
 hipError_t launch_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL>(a, splits, part, st);
+  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16>(a, splits, part, st);
   const bool g16 = a.group == 16;
   if (a.K % 128 == 0) {
     switch (a.group) {
-      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16>(a, splits, part, st);
-      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8>(a, splits, part, st);
-      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4>(a, splits, part, st);
-      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2>(a, splits, part, st);
+      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16>(a, splits, part, st);
+      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16>(a, splits, part, st);
+      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16>(a, splits, part, st);
+      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16>(a, splits, part, st);
     }
   }
-  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL>(a, splits, part, st) : launch_cfg<FM, FN, 1, 2, KTAIL>(a, splits, part, st);
+  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16>(a, splits, part, st)
+             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16>(a, splits, part, st);
 }
 
 template <int FM, int FN>
 hipError_t launch_tile(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  return a.K % kBK == 0 ? launch_meta<FM, FN, false>(a, splits, part, st) : launch_meta<FM, FN, true>(a, splits, part, st);
+  if (a.a_f16)
+    return a.K % kBK == 0 ? launch_meta<FM, FN, false, true>(a, splits, part, st)
+                          : launch_meta<FM, FN, true, true>(a, splits, part, st);
+  return a.K % kBK == 0 ? launch_meta<FM, FN, false, false>(a, splits, part, st)
+                        : launch_meta<FM, FN, true, false>(a, splits, part, st);
 }
 
 }  // namespace

@@ -15,7 +15,8 @@
 //   * a two-slot register pipeline runs over the flattened (row group, iteration)
 //     steps of a wave, so the next row's loads are in flight while a row finishes;
 //   * dequantization is v_fma_mix_f32 on nibbles masked into fp16 halves, bf16
-//     rounding by v_cvt_pk_bf16_f32, products by v_dot2_f32_bf16;
+//     rounding by v_cvt_pk_bf16_f32, products by v_dot2_f32_bf16 (fp16 activations:
+//     v_cvt_pk_f16_f32 rounding, products by v_dot2_f32_f16);
 //   * the R*M partial sums of a row group are reduced across the wave with a
 //     transposing butterfly on v_permlane32_swap / v_permlane16_swap and DPP row
 //     moves (no LDS round trips), parked in LDS, and written out at the end through
@@ -141,7 +142,8 @@ struct OutArg<true> {
   typedef Epi type;
 };
 
-template <int M, int R, int GPC, bool GEN>
+// F16: fp16 activations and an fp16 weight operand (else bf16).
+template <int M, int R, int GPC, bool GEN, bool F16>
 __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __restrict__ X,
                                                            const int32_t* __restrict__ packed,
                                                            const uint16_t* __restrict__ scales,
@@ -242,11 +244,11 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           uint32_t bw[4];
-          dq_word_bf16(st.w[r][w], dc[r][GPC == 2 ? w / 2 : 0], bw);
+          dq_word_op<F16>(st.w[r][w], dc[r][GPC == 2 ? w / 2 : 0], bw);
 #pragma unroll
           for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[r][m] = dot2_bf16(bw[i], xv[m][i], acc[r][m]);
+            for (int i = 0; i < 4; ++i) acc[r][m] = dot2_op<F16>(bw[i], xv[m][i], acc[r][m]);
         }
       }
       if (cit == pw - 1) {
@@ -340,9 +342,9 @@ int meta_row(const MmArgs& a) {
   return (int)(a.K / a.group);
 }
 
-template <int M, int R, int GPC, bool GEN>
+template <int M, int R, int GPC, bool GEN, bool F16>
 hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
-  auto k = gemv_kernel<M, R, GPC, GEN>;
+  auto k = gemv_kernel<M, R, GPC, GEN, F16>;
   static std::atomic<int> lds_set{64 * 1024};  // largest dynamic LDS size enabled so far
   if ((int)p.lds > lds_set.load()) {
     const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
@@ -358,18 +360,19 @@ hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int M, bool GEN>
+template <int M, bool GEN, bool F16>
 hipError_t run_g(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
   const bool g16 = a.mode == W4_MODE_GROUPWISE && a.group == 16;  // two groups per 32-code chunk
-  if (p.R == 2) return g16 ? run<M, 2, 2, GEN>(a, p, st) : run<M, 2, 1, GEN>(a, p, st);
-  return g16 ? run<M, 1, 2, GEN>(a, p, st) : run<M, 1, 1, GEN>(a, p, st);
+  if (p.R == 2) return g16 ? run<M, 2, 2, GEN, F16>(a, p, st) : run<M, 2, 1, GEN, F16>(a, p, st);
+  return g16 ? run<M, 1, 2, GEN, F16>(a, p, st) : run<M, 1, 1, GEN, F16>(a, p, st);
 }
 
 template <int M>
 hipError_t run_m(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
   const Epi& e = a.ep;
   const bool plain = e.nseg == 1 && e.dt == W4_DT_F32 && e.ld[0] == a.N;
-  return plain ? run_g<M, false>(a, p, st) : run_g<M, true>(a, p, st);
+  if (a.a_f16) return plain ? run_g<M, false, true>(a, p, st) : run_g<M, true, true>(a, p, st);
+  return plain ? run_g<M, false, false>(a, p, st) : run_g<M, true, false>(a, p, st);
 }
 
 }  // namespace

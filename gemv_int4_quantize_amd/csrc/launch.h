@@ -42,6 +42,7 @@ struct MmArgs {
   int mode;   // w4_mode
   int group;  // GROUPWISE g, else K
   bool transposed;
+  bool a_f16;  // activations (and the weight operand) fp16 instead of bf16
 };
 
 // Properties of the current device that kernel plans depend on.

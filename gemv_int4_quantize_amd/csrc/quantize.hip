@@ -225,9 +225,10 @@ __global__ __launch_bounds__(256) void quant_global_kernel(const void* __restric
   }
 }
 
-// Dequantize: bf16_rne(fp32(q - z) * s) or fp32(q - z) * s, the exact two-op
-// sequence (subtract, then multiply, each rounded) of the reference definition.
-template <bool BF16>
+// Dequantize: bf16_rne(fp32(q - z) * s), fp16_rne(fp32(q - z) * s) or fp32(q - z) * s,
+// the exact two-op sequence (subtract, then multiply, each rounded) of the reference
+// definition.  OUT: W4_DT_BF16, W4_DT_F16 or W4_DT_F32.
+template <int OUT>
 __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict__ packed,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ zeros, void* __restrict__ out,
@@ -250,10 +251,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
     const float d = qf - z;
     v[j] = d * s;
   }
-  if constexpr (BF16) {
+  if constexpr (OUT == W4_DT_BF16) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + gw);
+  } else if constexpr (OUT == W4_DT_F16) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_f16_bits(v[2 * i]) | ((uint32_t)f32_to_f16_bits(v[2 * i + 1]) << 16);
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out) + gw);
   } else {
     f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
@@ -328,9 +335,11 @@ hipError_t launch_dequantize(const int32_t* packed, const uint16_t* scales, cons
   const int wpgrp = mode == W4_MODE_GROUPWISE ? g / 8 : (int)wpr;
   const dim3 grid((unsigned)((total_words + 255) / 256)), block(256);
   if (out_dt == W4_DT_BF16)
-    dequant_kernel<true><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
+    dequant_kernel<W4_DT_BF16><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
+  else if (out_dt == W4_DT_F16)
+    dequant_kernel<W4_DT_F16><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
   else
-    dequant_kernel<false><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
+    dequant_kernel<W4_DT_F32><<<grid, block, 0, st>>>(packed, scales, zeros, out, total_words, wpr, kind, gpr, wpgrp);
   return hipGetLastError();
 }
 

@@ -34,8 +34,8 @@ def _ptr(t: torch.Tensor | None):
 
 
 def _as_bf16(a: torch.Tensor) -> torch.Tensor:
-    """Accept bf16 tensors or 16-bit integer tensors holding bf16 bits."""
-    if a.dtype == torch.bfloat16:
+    """Accept bf16 or fp16 activations, or 16-bit integer tensors holding bf16 bits."""
+    if a.dtype in (torch.bfloat16, torch.float16):
         return a
     if a.dtype in (torch.int16, torch.uint16):
         return a.view(torch.bfloat16)
@@ -168,10 +168,11 @@ def quantize_fused(parts, mode="groupwise", group: int | None = 128, zero: str =
 
 
 def dequantize(qw: QuantizedWeight, dtype=torch.bfloat16) -> torch.Tensor:
-    """w = bf16_rne((q - z) * s) (dtype bfloat16) or fp32 (q - z) * s (dtype float32), [N][K]."""
+    """w = bf16_rne((q - z) * s) (bfloat16), fp16_rne((q - z) * s) (float16) or fp32 (q - z) * s
+    (float32), [N][K]."""
     _need_cuda(qw.packed)
     out = torch.empty((qw.N, qw.K), dtype=dtype, device=qw.packed.device)
-    odt = {torch.bfloat16: DT_BF16, torch.float32: DT_F32}[dtype]
+    odt = {torch.bfloat16: DT_BF16, torch.float16: DT_F16, torch.float32: DT_F32}[dtype]
     desc = qw.desc()
     check(lib().w4_dequantize(_ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc), _ptr(out), odt,
                               _stream(out.device)))
@@ -215,7 +216,8 @@ def _mm_out(a: torch.Tensor, qw: QuantizedWeight, transposed: bool, bias, outs, 
         segs[i].ld = o.stride(0) if M > 1 else o.shape[1]
     ws, ws_bytes = _workspace(qw, M, transposed, split_k, a.device)
     desc = qw.desc()
-    check(lib().w4a16_mm_out(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
+    adt = DT_F16 if a.dtype == torch.float16 else DT_BF16
+    check(lib().w4a16_mm_out(_ptr(a), adt, M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(desc),
                              1 if transposed else 0, _ptr(bias), _ODT[dt], segs, len(outs), _ptr(ws), ws_bytes,
                              _stream(a.device)))
 
@@ -223,6 +225,8 @@ def _mm_out(a: torch.Tensor, qw: QuantizedWeight, transposed: bool, bias, outs, 
 def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: torch.Tensor | None = None,
        out: torch.Tensor | None = None, split_k: bool = True, out_dtype: torch.dtype | None = None) -> torch.Tensor:
     """W4A16 matmul: Y = A @ w^T (+bias) or, transposed, dX = A @ w (+bias), fp32 accumulation.
+
+    A is bfloat16 (the weight operand bf16_rne((q - z) * s)) or float16 (an fp16 weight operand).
 
     The output is fp32 unless `out_dtype` (or `out`) asks for bfloat16 / float16, rounded once
     to nearest even; the bias, when given, has the output dtype.  split_k lets a GEMM with few

@@ -113,7 +113,8 @@ int w4_quantize_pack_zp(const void* W, int w_dtype, const w4_desc* desc, int zer
                         void* ws, size_t ws_bytes, void* stream);
 
 /* Dequantize packed weights to out [N][K]: out_dtype W4_DT_BF16 writes the
- * matmul operand bf16_rne(fp32(q - z) * s), W4_DT_F32 writes fp32(q - z) * s.
+ * matmul operand bf16_rne(fp32(q - z) * s), W4_DT_F16 writes the fp16-activation
+ * operand fp16_rne(fp32(q - z) * s), W4_DT_F32 writes fp32(q - z) * s.
  * Bit-exact with the definition above.  out must be 16-byte aligned.  Source:
  * the dequantize() reference path of "Re-write HQQ Fused Gemm Transpose". */
 int w4_dequantize(const int32_t* packed, const uint16_t* scales, const uint16_t* zeros,
@@ -148,7 +149,9 @@ typedef struct {
   int64_t ld;
 } w4_out_seg;
 
-/* w4a16_mm with the output epilogue spelled out:
+/* w4a16_mm with the activation dtype and the output epilogue spelled out:
+ *   a_dtype W4_DT_BF16 (as w4a16_mm) or W4_DT_F16: fp16 activations multiply the
+ *   fp16 weight operand fp16_rne(fp32(q - z) * s), fp32 accumulation;
  *   out = out_rne(acc + bias[c]) for output column c, acc the fp32 sum;
  *   out_dtype W4_DT_F32, W4_DT_BF16 or W4_DT_F16 (round to nearest even);
  *   bias NULL or outc values (N non-transposed, K transposed) in out_dtype,
@@ -161,10 +164,10 @@ typedef struct {
  * ld = outc.  Sources: "[Kernel] Adding bias epilogue support for
  * cutlass_scaled_mm" (vLLM #5560: the bias in the output dtype); "Add fused QKV
  * HQQ triton_mm test" (pytorch/ao #306: one fused Q/K/V product). */
-int w4a16_mm_out(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
-                 const uint16_t* zeros, const w4_desc* desc, int transposed, const void* bias,
-                 int out_dtype, const w4_out_seg* segs, int nsegs, void* ws, size_t ws_bytes,
-                 void* stream);
+int w4a16_mm_out(const void* A, int a_dtype, int64_t M, const int32_t* packed,
+                 const uint16_t* scales, const uint16_t* zeros, const w4_desc* desc,
+                 int transposed, const void* bias, int out_dtype, const w4_out_seg* segs,
+                 int nsegs, void* ws, size_t ws_bytes, void* stream);
 
 /* Name of the kernel w4a16_mm would launch for these arguments ("gemv_m4",
  * "gemm_nt_256x128", "gemm_t_256x256_splitk4", ...) given the workspace

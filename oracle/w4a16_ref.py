@@ -46,7 +46,8 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
 * quantize with integer zero points: the same exact-rational brute force in
   AWQ's order (round, then add the integer zero), and invariants (integer zero
   in [0, 15], exact zero maps to code z and dequantizes to exactly 0).
-* dequantize: all 16 codes against an exact-rational bf16 rounding.
+* dequantize: all 16 codes against an exact-rational bf16 rounding (and fp16
+  rounding for the fp16 operand).
 * matmul: exact-rational triple loop on tiny shapes, one-hot pins of the layout
   in both modes, constant-code closed form, linearity and bias.
 * fused QKV: column concatenation (non-transposed) and sum (transposed).
@@ -64,7 +65,8 @@ import numpy as np
 __all__ = [
     "GLOBAL", "ROWWISE", "GROUPWISE", "MODE_NAMES",
     "meta_shape", "to_f32", "quantize", "pack", "unpack", "quantize_pack", "pack_bytes",
-    "dequantize_f32", "bf16_rne_bits", "bf16_bits_to_f64", "dequantize_bf16_bits",
+    "dequantize_f32", "bf16_rne_bits", "bf16_bits_to_f64", "dequantize_bf16_bits", "f16_bits_to_f64",
+    "dequantize_f16_bits",
     "matmul", "round_output", "fuse_rows", "mae", "compression_ratio", "page_compression_ratio",
 ]
 
@@ -236,8 +238,20 @@ def dequantize_bf16_bits(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarr
     return bf16_rne_bits(dequantize_f32(packed, scales, zeros, K))
 
 
+def f16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """fp16 bit patterns -> float64 (exact)."""
+    return np.asarray(b, dtype=np.uint16).view(_F16).astype(np.float64)
+
+
+def dequantize_f16_bits(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int) -> np.ndarray:
+    """The fp16 weight operand ``fp16_rne((q - z) * s)`` (the fp32 two-op sequence, then one
+    rounding to fp16) as uint16 bits: the operand of fp16 activations."""
+    with np.errstate(over="ignore"):
+        return dequantize_f32(packed, scales, zeros, K).astype(_F16).view(np.uint16)
+
+
 def matmul(a_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, K: int,
-           transposed: bool = False, bias: np.ndarray | None = None) -> np.ndarray:
+           transposed: bool = False, bias: np.ndarray | None = None, a_dtype: str = "bf16") -> np.ndarray:
     """float64 result of the W4A16 matmul.
 
     Non-transposed (Objective 2 of "Quantized LLM Inference with Triton
@@ -246,9 +260,15 @@ def matmul(a_bf16: np.ndarray, packed: np.ndarray, scales: np.ndarray, zeros: np
     ``dX[m, k] = sum_n dY[m, n] * w[n, k] (+ bias[k])`` with dY bf16 [M][N].
     ``w`` is the bf16 dequantized weight; the bias is fp32 ("[Kernel] Adding
     bias epilogue support for cutlass_scaled_mm").  Accumulates in float64.
+    ``a_dtype="f16"``: the activations are fp16 bits and the weight operand is
+    ``dequantize_f16_bits`` (the fp16 path of a W4A16 kernel).
     """
-    w64 = bf16_bits_to_f64(dequantize_bf16_bits(packed, scales, zeros, K))   # [N][K]
-    a64 = bf16_bits_to_f64(a_bf16)
+    if a_dtype == "f16":
+        w64 = f16_bits_to_f64(dequantize_f16_bits(packed, scales, zeros, K))
+        a64 = f16_bits_to_f64(a_bf16)
+    else:
+        w64 = bf16_bits_to_f64(dequantize_bf16_bits(packed, scales, zeros, K))   # [N][K]
+        a64 = bf16_bits_to_f64(a_bf16)
     y = a64 @ w64 if transposed else a64 @ w64.T
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]

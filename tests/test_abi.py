@@ -127,7 +127,7 @@ def test_quantize_validation_before_launch():
     assert qz(a16, 1, ctypes.byref(d), _lib.ZERO_INT, ctypes.c_void_p(0x10002), a16, a16, None, 0, None) == \
         _lib.W4_ERR_ALIGN
     dq = L.w4_dequantize
-    assert dq(a16, a16, a16, ctypes.byref(d), a16, _lib.DT_F16, None) == _lib.W4_ERR_INVALID
+    assert dq(a16, a16, a16, ctypes.byref(d), a16, 7, None) == _lib.W4_ERR_INVALID
     assert dq(a16, a16, a16, ctypes.byref(d), ctypes.c_void_p(0x10004), _lib.DT_BF16, None) == _lib.W4_ERR_ALIGN
 
 
@@ -148,13 +148,14 @@ def test_mm_out_validation_before_launch():
     d = _lib.W4Desc(64, 128, _lib.MODE_ROWWISE, 0)
     a16 = ctypes.c_void_p(0x10000)
 
-    def call(segs, nsegs, dt=_lib.DT_BF16, M=4, bias=None, transposed=0):
+    def call(segs, nsegs, dt=_lib.DT_BF16, M=4, bias=None, transposed=0, adt=_lib.DT_BF16):
         arr = (_lib.W4OutSeg * max(1, len(segs)))(*[_lib.W4OutSeg(*s) for s in segs]) if segs else None
-        return L.w4a16_mm_out(a16, M, a16, a16, a16, ctypes.byref(d), transposed, bias, dt, arr, nsegs,
+        return L.w4a16_mm_out(a16, adt, M, a16, a16, a16, ctypes.byref(d), transposed, bias, dt, arr, nsegs,
                               None, 0, None)
 
     ok3 = [(0x20000, 32, 32), (0x30000, 16, 16), (0x40000, 16, 20)]
     assert call(ok3, 3, dt=7) == _lib.W4_ERR_INVALID                       # unknown dtype
+    assert call(ok3, 3, adt=_lib.DT_F32) == _lib.W4_ERR_INVALID            # activations bf16 or fp16 only
     assert call(ok3, 0) == _lib.W4_ERR_INVALID                             # no segments
     assert call(ok3 + [(0x50000, 1, 1)] * 2, 5) == _lib.W4_ERR_INVALID     # more than four
     assert call([(0x20000, 32, 32), (0x30000, 16, 16)], 2) == _lib.W4_ERR_INVALID  # 48 != N

@@ -83,3 +83,58 @@ def test_int8_word_view_and_wrap():
                                             "groupwise", 64)
     x = synth.activations_bf16(733, 0, M, K)
     assert_mm_close(host(w4.mm(dev_bf16(x), wrapped)), O.matmul(x, O.pack(q), s, z, K), "int8-wrapped weight")
+
+
+def _acts_f16(cfg, idx, M, L):
+    """Synthetic activations as fp16 bits (the bf16 draw, rounded to fp16)."""
+    a = O.bf16_bits_to_f64(synth.activations_bf16(cfg, idx, M, L))
+    return a.astype(np.float16).view(np.uint16)
+
+
+def _dev_f16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.float16)
+
+
+@pytest.mark.parametrize("mode,g", [("rowwise", None), ("groupwise", 64), ("groupwise", 16)],
+                         ids=["rowwise", "g64", "g16"])
+def test_dequantize_f16_bit_exact(mode, g):
+    N, K = 300, 2048
+    w = synth.weight(734, 0, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
+    got = w4.dequantize(qw, torch.float16).view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, O.dequantize_f16_bits(*ref, K))
+
+
+F16_CASES = [(1, False), (2, False), (3, False), (4, False), (37, False), (300, False), (128, True), (300, True)]
+
+
+@pytest.mark.parametrize("M,tr", F16_CASES, ids=[f"{m}{'t' if t else ''}" for m, t in F16_CASES])
+@pytest.mark.parametrize("mode,g", [("rowwise", None), ("groupwise", 64), ("groupwise", 16)],
+                         ids=["rowwise", "g64", "g16"])
+def test_f16_activations(M, tr, mode, g):
+    """fp16 activations times the fp16 weight operand, fp32 accumulation, on every path."""
+    N, K = 264, 2048
+    print(f"[case] f16 activations M={M} t={tr} {mode}{g or ''}", flush=True)
+    w = synth.weight(735, M, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
+    a = _acts_f16(735, M, M, N if tr else K)
+    bias = synth.bias_f32(735, M, K if tr else N)
+    y = w4.mm(_dev_f16(a), qw, transposed=tr, bias=dev_f32(bias))
+    assert_mm_close(host(y), O.matmul(a, *ref, K, tr, bias=bias, a_dtype="f16"), f"f16 M={M} t={tr} {mode}{g}")
+
+
+def test_f16_activations_split_k_and_bf16_out():
+    """fp16 activations on a split-K GEMM, written as bf16 through the epilogue."""
+    M, N, K = 128, 2048, 8192
+    w = synth.weight(736, 0, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), O.GROUPWISE, 128)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), "groupwise", 128)
+    assert "splitk" in w4.kernel_for(M, N, K, "groupwise", 128)
+    a = _acts_f16(736, 0, M, K)
+    y = w4.mm(_dev_f16(a), qw)
+    ref64 = O.matmul(a, *ref, K, a_dtype="f16")
+    assert_mm_close(host(y), ref64, "f16 split-K")
+    yb = w4.mm(_dev_f16(a), qw, out_dtype=torch.bfloat16)
+    assert torch.equal(yb, y.to(torch.bfloat16))

@@ -56,6 +56,13 @@ def test_dequant_all_codes_exact(s16, z16):
         assert int(bits[c]) == _exact_deq_bits(c, s16, z16), (c, s16, z16)
         d = round_fmt(Fraction(c) - frac(z16), "f32")
         assert Fraction(float(f32[c])) == round_fmt(d * frac(s16), "f32"), (c, s16, z16)
+    # the fp16 operand: the same fp32 value rounded once more, to fp16
+    b16 = O.dequantize_f16_bits(packed, scales, zeros, 8).reshape(-1)
+    for c in range(16):
+        d = round_fmt(Fraction(c) - frac(z16), "f32")
+        want = round_fmt(round_fmt(d * frac(s16), "f32"), "f16")
+        got = O.f16_bits_to_f64(np.array([b16[c]]))[0]
+        assert (Fraction(got) if np.isfinite(got) else got) == want, (c, s16, z16)
 
 
 def test_bf16_rounding_ties_and_specials():
