@@ -8,6 +8,8 @@ from ._lib import LIB_PATH, W4Desc, W4Error, lib  # noqa: F401
 from .ops import (  # noqa: F401
     QuantizedWeight,
     dequantize,
+    deserialize,
+    load,
     empty_quantized,
     kernel_for,
     meta_shape,
@@ -17,6 +19,8 @@ from .ops import (  # noqa: F401
     quantize_fused,
     quantize_pack,
     quantize_pack_into,
+    save,
+    serialize,
 )
 from .layer import W4A16Linear, w4a16_linear  # noqa: F401
 

@@ -26,7 +26,8 @@ ZERO_FP16, ZERO_INT = 0, 1
 # every entry point declared in include/w4a16.h
 EXPORTS = (
     "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize", "w4a16_mm",
-    "w4a16_mm_out", "w4a16_mm_kernel", "w4_status_string", "w4_last_error", "w4_version",
+    "w4a16_mm_out", "w4a16_mm_kernel", "w4_serial_layout", "w4_serial_parse", "w4_status_string", "w4_last_error",
+    "w4_version",
 )
 
 
@@ -36,6 +37,15 @@ class W4Desc(ctypes.Structure):
 
 class W4OutSeg(ctypes.Structure):
     _fields_ = [("Y", ctypes.c_void_p), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+class W4SerialHeader(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_char * 8), ("version", ctypes.c_uint32), ("header_bytes", ctypes.c_uint32),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("mode", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("zero_kind", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("packed_offset", ctypes.c_uint64), ("packed_bytes", ctypes.c_uint64),
+                ("scales_offset", ctypes.c_uint64), ("zeros_offset", ctypes.c_uint64), ("meta_bytes", ctypes.c_uint64),
+                ("total_bytes", ctypes.c_uint64), ("reserved", ctypes.c_uint8 * 32)]
 
 
 class W4Error(RuntimeError):
@@ -69,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.w4a16_mm.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp, sz, vp]
     L.w4a16_mm_out.argtypes = [vp, i32, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz,
                                vp]
+    L.w4_serial_layout.argtypes = [pdesc, i32, ctypes.POINTER(W4SerialHeader)]
+    L.w4_serial_parse.argtypes = [vp, sz, pdesc, ctypes.POINTER(ctypes.c_int)]
     L.w4a16_mm_kernel.argtypes = [i64, pdesc, i32]
     L.w4a16_mm_kernel.restype = ctypes.c_char_p
     L.w4_status_string.argtypes = [i32]
@@ -78,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.w4_version.argtypes = []
     L.w4_version.restype = ctypes.c_char_p
     for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize",
-                 "w4a16_mm", "w4a16_mm_out"):
+                 "w4a16_mm", "w4a16_mm_out", "w4_serial_layout", "w4_serial_parse"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -295,6 +295,60 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   return w4::gemm_name(a, device_caps(), true);
 }
 
+static_assert(sizeof(w4_serial_header) == 128, "the serialized header is 128 bytes");
+
+int w4_serial_layout(const w4_desc* desc, int zero_kind, w4_serial_header* hdr) {
+  if (hdr == nullptr) return fail(W4_ERR_INVALID, "hdr is NULL");
+  int s = check_desc(desc);
+  if (s != W4_OK) return s;
+  if (zero_kind != W4_ZERO_FP16 && zero_kind != W4_ZERO_INT)
+    return fail(W4_ERR_INVALID, "zero_kind = %d is not W4_ZERO_FP16 or W4_ZERO_INT", zero_kind);
+  int64_t pairs = 0;
+  s = w4_meta_pairs(desc, &pairs);
+  if (s != W4_OK) return s;
+  auto up64 = [](uint64_t x) { return (x + 63) & ~(uint64_t)63; };
+  w4_serial_header h;
+  memset(&h, 0, sizeof(h));
+  memcpy(h.magic, W4_SERIAL_MAGIC, sizeof(W4_SERIAL_MAGIC));
+  h.version = W4_SERIAL_VERSION;
+  h.header_bytes = sizeof(w4_serial_header);
+  h.N = desc->N;
+  h.K = desc->K;
+  h.mode = desc->mode;
+  h.group = desc->mode == W4_MODE_GROUPWISE ? desc->group : 0;
+  h.zero_kind = zero_kind;
+  h.packed_offset = up64(sizeof(w4_serial_header));
+  h.packed_bytes = (uint64_t)desc->N * (uint64_t)(desc->K / 8) * 4;
+  h.meta_bytes = (uint64_t)pairs * 2;
+  h.scales_offset = up64(h.packed_offset + h.packed_bytes);
+  h.zeros_offset = up64(h.scales_offset + h.meta_bytes);
+  h.total_bytes = up64(h.zeros_offset + h.meta_bytes);
+  *hdr = h;
+  return ok();
+}
+
+int w4_serial_parse(const void* bytes, size_t len, w4_desc* desc, int* zero_kind) {
+  if (bytes == nullptr || desc == nullptr || zero_kind == nullptr)
+    return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  if (len < sizeof(w4_serial_header))
+    return fail(W4_ERR_INVALID, "%zu bytes cannot hold the %zu-byte header", len, sizeof(w4_serial_header));
+  w4_serial_header h;
+  memcpy(&h, bytes, sizeof(h));
+  if (memcmp(h.magic, W4_SERIAL_MAGIC, sizeof(W4_SERIAL_MAGIC)) != 0) return fail(W4_ERR_INVALID, "bad magic");
+  if (h.version != W4_SERIAL_VERSION) return fail(W4_ERR_INVALID, "version %u is not %d", h.version, W4_SERIAL_VERSION);
+  const w4_desc d = {h.N, h.K, h.mode, h.group};
+  w4_serial_header want;
+  int s = w4_serial_layout(&d, h.zero_kind, &want);
+  if (s != W4_OK) return s;
+  if (memcmp(&h, &want, sizeof(h)) != 0) return fail(W4_ERR_INVALID, "header sizes or offsets do not match the layout");
+  if (h.total_bytes > len)
+    return fail(W4_ERR_INVALID, "the weight needs %llu bytes, %zu are available", (unsigned long long)h.total_bytes,
+                len);
+  *desc = d;
+  *zero_kind = h.zero_kind;
+  return ok();
+}
+
 const char* w4_status_string(int status) {
   switch (status) {
     case W4_OK: return "W4_OK";

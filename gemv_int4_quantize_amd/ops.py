@@ -59,6 +59,7 @@ class QuantizedWeight:
     K: int
     mode: int
     group: int
+    zero: str = "fp16"  # "fp16" zero points, or "int" (integer zero points in [0, 15])
 
     def desc(self) -> W4Desc:
         return W4Desc(self.N, self.K, self.mode, self.group if self.mode == MODE_GROUPWISE else 0)
@@ -149,6 +150,7 @@ def quantize_pack(W: torch.Tensor, mode="groupwise", group: int | None = 128, ze
     integer zero points (AWQ style)."""
     N, K = W.shape
     qw = empty_quantized(N, K, mode, group, W.device)
+    qw.zero = zero
     quantize_pack_into(W, qw, 0, zero)
     return qw
 
@@ -160,11 +162,59 @@ def quantize_fused(parts, mode="groupwise", group: int | None = 128, zero: str =
     if mode_id(mode) == MODE_GLOBAL:
         raise ValueError("GLOBAL scale / zero cannot be fused by rows")
     qw = empty_quantized(N, K, mode, group, parts[0].device)
+    qw.zero = zero
     r = 0
     for p in parts:
         quantize_pack_into(p, qw, r, zero)
         r += p.shape[0]
     return qw
+
+
+def serialize(qw: QuantizedWeight) -> bytes:
+    """The packed weight in the library's serialized form (w4_serial_header, then the packed
+    words, scales and zeros at 64-byte aligned offsets); device tensors are copied to host."""
+    hdr = _lib.W4SerialHeader()
+    check(lib().w4_serial_layout(ctypes.byref(qw.desc()), _ZERO[qw.zero], ctypes.byref(hdr)))
+    buf = bytearray(hdr.total_bytes)
+    buf[:ctypes.sizeof(hdr)] = bytes(hdr)
+    for off, t, n in ((hdr.packed_offset, qw.packed, hdr.packed_bytes), (hdr.scales_offset, qw.scales, hdr.meta_bytes),
+                      (hdr.zeros_offset, qw.zeros, hdr.meta_bytes)):
+        b = t.contiguous().cpu().view(torch.uint8).numpy().tobytes()
+        assert len(b) == n
+        buf[off:off + n] = b
+    return bytes(buf)
+
+
+def deserialize(data: bytes, device="cuda") -> QuantizedWeight:
+    """Inverse of :func:`serialize`: validate the header and upload the sections to `device`."""
+    data = bytes(data)
+    desc = W4Desc()
+    zk = ctypes.c_int(0)
+    cbuf = ctypes.create_string_buffer(data, len(data))
+    check(lib().w4_serial_parse(cbuf, len(data), ctypes.byref(desc), ctypes.byref(zk)))
+    hdr = _lib.W4SerialHeader.from_buffer_copy(data[:ctypes.sizeof(_lib.W4SerialHeader)])
+    N, K, m = desc.N, desc.K, desc.mode
+    g = desc.group if m == MODE_GROUPWISE else 0
+    shp = meta_shape(N, K, m, g)
+
+    def section(off, n, dtype, shape):
+        return torch.frombuffer(bytearray(data[off:off + n]), dtype=dtype).reshape(shape).to(device)
+
+    return QuantizedWeight(
+        packed=section(hdr.packed_offset, hdr.packed_bytes, torch.int32, (N, K // 8)),
+        scales=section(hdr.scales_offset, hdr.meta_bytes, torch.float16, shp),
+        zeros=section(hdr.zeros_offset, hdr.meta_bytes, torch.float16, shp),
+        N=N, K=K, mode=m, group=g, zero={v: k for k, v in _ZERO.items()}[zk.value])
+
+
+def save(qw: QuantizedWeight, path: str) -> None:
+    with open(path, "wb") as f:
+        f.write(serialize(qw))
+
+
+def load(path: str, device="cuda") -> QuantizedWeight:
+    with open(path, "rb") as f:
+        return deserialize(f.read(), device)
 
 
 def dequantize(qw: QuantizedWeight, dtype=torch.bfloat16) -> torch.Tensor:

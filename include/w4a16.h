@@ -174,6 +174,39 @@ int w4a16_mm_out(const void* A, int a_dtype, int64_t M, const int32_t* packed,
  * w4_workspace_bytes reports, or NULL when they are invalid.  Host only. */
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed);
 
+/* Serialized packed weight: this 128-byte little-endian header, then the packed
+ * words [N][K/8] int32, the scales and the zeros (fp16 bits, w4_meta_pairs each),
+ * every section starting at a 64-byte aligned offset from the start of the
+ * header.  The packed words are also the INT8 packing of Objective 1 of
+ * "Quantized LLM Inference with Triton Kernels" read as bytes. */
+#define W4_SERIAL_MAGIC "W4A16PK"
+#define W4_SERIAL_VERSION 1
+typedef struct {
+  char magic[8];          /* W4_SERIAL_MAGIC, NUL-terminated */
+  uint32_t version;       /* W4_SERIAL_VERSION */
+  uint32_t header_bytes;  /* 128 */
+  int64_t N, K;
+  int32_t mode, group;    /* as in w4_desc */
+  int32_t zero_kind;      /* w4_zero_kind the zeros were made with */
+  int32_t reserved0;
+  uint64_t packed_offset, packed_bytes;
+  uint64_t scales_offset, zeros_offset, meta_bytes;
+  uint64_t total_bytes;   /* header + sections, a multiple of 64 */
+  uint8_t reserved[32];
+} w4_serial_header;
+
+/* Fill *hdr for a weight of this descriptor and zero kind (sizes and offsets
+ * included; reserved bytes zero).  Host only; W4_ERR_INVALID on a bad
+ * descriptor, zero kind or NULL. */
+int w4_serial_layout(const w4_desc* desc, int zero_kind, w4_serial_header* hdr);
+
+/* Check a serialized header read from `bytes` (at least `len` bytes available)
+ * and return its descriptor and zero kind: the magic, version, descriptor,
+ * section sizes, 64-byte alignment, ordering and total size must all match what
+ * w4_serial_layout gives, and total_bytes must not exceed len.  Host only;
+ * W4_ERR_INVALID on any mismatch or NULL. */
+int w4_serial_parse(const void* bytes, size_t len, w4_desc* desc, int* zero_kind);
+
 /* Human-readable name of a status code. */
 const char* w4_status_string(int status);
 

@@ -138,3 +138,18 @@ def test_f16_activations_split_k_and_bf16_out():
     assert_mm_close(host(y), ref64, "f16 split-K")
     yb = w4.mm(_dev_f16(a), qw, out_dtype=torch.bfloat16)
     assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+def test_serialized_weight_round_trip(tmp_path):
+    """A weight quantized on the GPU, saved and loaded back, multiplies bit-identically."""
+    N, K, M = 520, 2048, 300
+    w = synth.weight(737, 0, N, K, "bf16")
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), "groupwise", 128, zero="int")
+    path = str(tmp_path / "w.w4")
+    w4.save(qw, path)
+    back = w4.load(path, device=DEV)
+    assert back.zero == "int" and (back.N, back.K, back.group) == (N, K, 128)
+    x = dev_bf16(synth.activations_bf16(737, 0, M, K))
+    assert torch.equal(w4.mm(x, back), w4.mm(x, qw))
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), O.GROUPWISE, 128, int_zero=True)
+    assert_quant_equal(back, *ref, what="loaded weight")
