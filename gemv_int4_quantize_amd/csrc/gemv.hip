@@ -23,7 +23,6 @@
 //     the output epilogue (bias, output dtype, output segments).
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 
 #include "common.h"
 #include "epilogue.h"
@@ -151,32 +150,25 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ zeros,
                                                            const typename OutArg<GEN>::type ep,
                                                            int N, int K, int meta_row, int geo) {
-  // geo packs log2g (bits 0-4), rows_per_block (5-15), phase_iters (16-23) and log2 of the
-  // split S (24-27): with the plain output the whole argument block is one 64-byte line
-  const int log2g = geo & 31, rows_per_block = (geo >> 5) & 2047, phase_iters = (geo >> 16) & 255;
-  const int log2s = (geo >> 24) & 15;
+  // geo packs log2g (bits 0-4), rows_per_block (5-15) and phase_iters (16-30): with the
+  // plain output the whole argument block is one 64-byte line
+  const int log2g = geo & 31, rows_per_block = (geo >> 5) & 2047, phase_iters = geo >> 16;
   extern __shared__ u32x4 smem[];
   constexpr int T = kWaves * 64;
   const int KS = K >> 5;               // 16-byte chunks per row
   const int iters = (KS + 63) >> 6;    // 2048-column iterations per row
   const int PW = phase_iters;          // iterations whose X is resident at a time
   u32x4* xs = smem;                                             // [PW][M][4 words][64 chunks]
-  float* outs = reinterpret_cast<float*>(smem + PW * M * 256);  // [S][rows_per_block][M]
+  float* outs = reinterpret_cast<float*>(smem + PW * M * 256);  // [rows_per_block][M]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Split: with fewer row groups than waves, S waves share a row group, wave slice s taking
-  // iterations s, s + S, ... of each phase and summing into its own partial slot.
-  const int S = 1 << log2s;
-  const int WG = kWaves >> log2s;  // waves per slice
-  const int sl = wave / WG, rgw = wave - sl * WG;
   const int r0 = blockIdx.x * rows_per_block;
   const int r1 = min(r0 + rows_per_block, N);
   const int KW = K >> 3;
   const uint32_t meta_bytes = meta_row > 0 ? (uint32_t)meta_row * 2 : 2u;
-  // row groups rg = rgw, rgw + WG, ... of R rows each
+  // row groups rg = wave, wave + 16, ... of R rows each
   const int nrg = (r1 - r0 + R - 1) / R;
-  const int my_rg = nrg > rgw ? (nrg - rgw + WG - 1) / WG : 0;
-  for (int u = tid; u < S * rows_per_block * M; u += kWaves * 64) outs[u] = 0.0f;
+  const int my_rg = nrg > wave ? (nrg - wave + kWaves - 1) / kWaves : 0;
 
   const uint32_t vo = lane * 16;
   uint32_t vs[GPC];
@@ -186,7 +178,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
   // Loads of step (row group k, iteration it); a row group past this wave's last one, or
   // a row past the block, gets a zero-sized resource and reads zeros without a request.
   auto load = [&](int k, int it, Stage<R, GPC>& st) {
-    const int rg = rgw + k * WG;
+    const int rg = wave + k * kWaves;
     const uint32_t so = ((uint32_t)(it * 2048) >> log2g) * 2;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -214,17 +206,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
   Stage<R, GPC> A, B;
   for (int p0 = 0; p0 < iters; p0 += PW) {
     const int pw = min(PW, iters - p0);
-    const int mine = pw > sl ? (pw - sl + S - 1) >> log2s : 0;  // this slice's iterations
-    const int steps = my_rg * mine;
-    // the slice's last iteration of the phase, as an equality test: an inequality here
-    // doubled the kernel's register count
-    const int last = sl + (mine - 1) * S;
-    // step t of this phase -> (row group k = t / mine, iteration p0 + sl + S (t % mine))
-    int lk = 0, lit = sl, ck = 0, cit = sl;
+    const int steps = my_rg * pw;
+    // step t of this phase -> (row group k = t / pw, iteration p0 + t % pw)
+    int lk = 0, lit = 0, ck = 0, cit = 0;
     auto advance = [&](int& k, int& it) {
-      it += S;
-      if (it >= pw) {
-        it = sl;
+      if (++it == pw) {
+        it = 0;
         ++k;
       }
     };
@@ -264,8 +251,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
             for (int i = 0; i < 4; ++i) acc[r][m] = dot2_op<F16>(bw[i], xv[m][i], acc[r][m]);
         }
       }
-      if (cit == last) {
-        // this slice's part of the phase is done: reduce across the wave, accumulate in LDS
+      if (cit == pw - 1) {
+        // this phase of the row group is done: reduce across the wave, accumulate in LDS
         constexpr int MP = M == 3 ? 4 : M;
         constexpr int V = R * MP;
         constexpr int LOGV = V == 1 ? 0 : V == 2 ? 1 : V == 4 ? 2 : V == 8 ? 3 : 4;
@@ -278,10 +265,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
         constexpr int SPAN = 64 / V;
         const int idx = lane >> (6 - LOGV);
         const int r = idx / MP, m = idx - (idx / MP) * MP;
-        const int lr = (rgw + ck * WG) * R + r;  // row within the block
+        const int lr = (wave + ck * kWaves) * R + r;  // row within the block
         if ((lane & (SPAN - 1)) == 0 && m < M && r0 + lr < r1) {
-          float* o = outs + (sl * rows_per_block + lr) * M + m;  // one wave per (slice, row, m)
-          *o += sum;
+          float* o = outs + lr * M + m;  // each (row, m) belongs to one wave: no race
+          *o = p0 == 0 ? sum : *o + sum;
         }
 #pragma unroll
         for (int rr = 0; rr < R; ++rr)
@@ -312,17 +299,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
     for (int u = tid; u < (r1 - r0) * M; u += T) {
       const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
       const int n = r0 + lr;
-      float v = outs[lr * M + m];
-      for (int q = 1; q < S; ++q) v += outs[(q * rows_per_block + lr) * M + m];  // fixed order
-      Y[(size_t)m * N + n] = v + (bias != nullptr ? bias[n] : 0.0f);
+      Y[(size_t)m * N + n] = outs[lr * M + m] + (bias != nullptr ? bias[n] : 0.0f);
     }
   } else {
     for (int u = tid; u < (r1 - r0) * M; u += T) {
       const int m = u / (r1 - r0), lr = u - m * (r1 - r0);
       const int n = r0 + lr;
-      float v = outs[lr * M + m];
-      for (int q = 1; q < S; ++q) v += outs[(q * rows_per_block + lr) * M + m];
-      epi_put(ep, epi_col(ep, n), m, v);
+      epi_put(ep, epi_col(ep, n), m, outs[lr * M + m]);
     }
   }
 }
@@ -331,7 +314,6 @@ struct GemvPlan {
   int R;
   int blocks, rows_per_block;
   int phase_iters;
-  int log2s;  // waves sharing a row group (split of its iterations), log2
   size_t lds;
 };
 
@@ -347,19 +329,9 @@ GemvPlan plan(const MmArgs& a, const DeviceCaps& caps) {
   p.rows_per_block = (int)((a.N + p.blocks - 1) / p.blocks);
   if (p.rows_per_block > 1024) p.rows_per_block = 1024;
   p.blocks = (int)((a.N + p.rows_per_block - 1) / p.rows_per_block);
-  // Fewer row groups than waves: split each row group's iterations over S waves, so every
-  // wave streams (W4A16_GEMV_SPLIT caps S, an A/B benchmarking override).
-  static const int split_cap = [] {
-    const char* e = getenv("W4A16_GEMV_SPLIT");
-    return e != nullptr ? atoi(e) : kWaves;
-  }();
-  const int rgs = (p.rows_per_block + p.R - 1) / p.R;
-  p.log2s = 0;
-  while ((2 << p.log2s) <= split_cap && rgs * (2 << p.log2s) <= kWaves && (2 << p.log2s) <= iters) ++p.log2s;
-  const size_t outs = ((size_t)p.rows_per_block * a.M * 4) << p.log2s;
+  const size_t outs = (size_t)p.rows_per_block * a.M * 4;
   const size_t budget = caps.lds > outs ? caps.lds - outs : 0;
   p.phase_iters = (int)std::min<size_t>((size_t)iters, budget / x_iter);
-  while (p.log2s > 0 && (1 << p.log2s) > p.phase_iters) --p.log2s;  // a slice per resident iteration
   p.lds = (size_t)p.phase_iters * x_iter + outs;
   return p;
 }
@@ -384,8 +356,7 @@ hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
   if constexpr (GEN) out = a.ep;
   else out = PlainOut{static_cast<const float*>(a.ep.bias), static_cast<float*>(a.ep.y[0])};
   k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, out, (int)a.N, (int)a.K,
-                                           meta_row(a),
-                                           log2g | (p.rows_per_block << 5) | (p.phase_iters << 16) | (p.log2s << 24));
+                                           meta_row(a), log2g | (p.rows_per_block << 5) | (p.phase_iters << 16));
   return hipGetLastError();
 }
 
