@@ -16,8 +16,13 @@
 //     operand slot 8 h + t (h = lane / 32) is contraction index k0 + 32 h + 8 kk + t, so a
 //     lane's four words for the step are contiguous; the activation fragment is read from
 //     LDS with the same mapping;
-//   * activation tiles: global -> VGPR -> LDS (two buffers, rows padded by 16 bytes),
-//     loaded two steps ahead; weight words one step ahead; one barrier per step;
+//   * activation tiles: global -> LDS with direct loads (buffer_load ... lds: no staging
+//     registers, no LDS store instructions), two buffers, the next step's tile in flight
+//     while a step computes; the 16-byte chunks of a 128-byte row are XOR-swizzled so the
+//     32 rows a fragment read touches fall in distinct banks.  When K % 64 != 0 the tile
+//     goes global -> VGPR -> LDS instead (rows padded by 16 bytes, loaded two steps
+//     ahead), so the columns past K can be zeroed.  Weight words one step ahead; one
+//     barrier per step;
 //   * inside a step, the LDS fragments and the dequantized words of sub-step kk+1 are
 //     produced while the MFMAs of kk issue;
 //   * scale / zero: rowwise and global modes load them once; groupwise loads, once per
@@ -52,7 +57,7 @@ constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
 // (2 when g = 16).  KTAIL: K % 64 != 0 (activation columns past K are zeroed in LDS).
 // WB (META 1): bytes of one wide load = 2 max(1, 128 / g), a compile-time width so that the
 // loop holds exactly one load form.
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA>
 __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -62,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
                                                          int kt_per_slice, float* __restrict__ part) {
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   constexpr int AU = BM * 8 / 256;  // 16-byte activation units per thread per step
+  static_assert(!(DMA && KTAIL), "direct LDS loads cannot zero the columns past K");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* As0 = smem;
   uint16_t* As1 = smem + BM * kLR;
@@ -75,11 +81,14 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 
   // activations: one resource over the tile's rows (rows past M read as zero)
   const rsrc_t ar = make_rsrc(A + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  // DMA: LDS slot u (16 bytes) of a buffer holds row u / 8, chunk (u % 8) ^ ((u / 32) % 8)
+  // of the tile: the XOR keeps the 32 rows of a fragment read in distinct 16-byte banks
   uint32_t a_off[AU];
 #pragma unroll
   for (int i = 0; i < AU; ++i) {
     const int u = tid + i * 256;
-    a_off[i] = (uint32_t)((u >> 3) * K * 2 + (u & 7) * 16);
+    const int ch = DMA ? ((u & 7) ^ ((u >> 5) & 7)) : (u & 7);
+    a_off[i] = (uint32_t)((u >> 3) * K * 2 + ch * 16);
   }
   // weights: this wave's 32 FN rows (rows past N read as zero)
   const int n0w = c0 + wave * FN * 32;
@@ -184,9 +193,16 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     }
   };
   auto read_a = [&](const uint16_t* buf, int kk, u32x4 (&af)[FM]) {
-    const uint16_t* as = buf + lr * kLR + h * 32 + kk * 8;
+    if constexpr (DMA) {
+      // row i 32 + lr, chunk (4 h + kk) ^ ((lr / 4) % 8) of a 128-byte row
+      const char* as = reinterpret_cast<const char*>(buf) + lr * 128 + (((4 * h + kk) ^ ((lr >> 2) & 7)) << 4);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * kLR);
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * 128);
+    } else {
+      const uint16_t* as = buf + lr * kLR + h * 32 + kk * 8;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * kLR);
+    }
   };
   auto compute = [&](const BRegs& B, const DqConst (&dc)[FN][GPW], const uint16_t* buf) {
     u32x4 af[2][FM], bfr[2][FN];
@@ -238,6 +254,70 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     }
   }
   // steps KB + t; loads past the slice read other (finite) data or zeros and are never used
+  if constexpr (DMA) {
+    // Activation tiles go global -> LDS directly (buffer_load ... lds, no registers, no LDS
+    // store instructions) into two buffers: the tile of step t + 1 is loaded while step t
+    // computes.  Each step issues its weight (and scale / zero) loads, then the tile loads.
+    constexpr int BUFB = BM * 128;  // bytes per buffer
+    typedef __attribute__((address_space(3))) void lds_void;
+    char* lds = reinterpret_cast<char*>(smem);
+    auto dma = [&](int kt, int buf) {
+#pragma unroll
+      for (int i = 0; i < AU; ++i)
+        // the whole offset in the range-checked vector offset: reads past the tile's rows
+        // (steps past the slice, rows past M) return zeros.  The explicit int matters: with
+        // an unsigned argument the host pass silently drops the kernel's launch stub.
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(lds + buf * BUFB + (i * 256 + wave * 64) * 16), 16,
+                                                 (int)(a_off[i] + kt * kBK * 2), 0, 0, 0);
+    };
+    // Barrier once every load of this wave has landed (s_waitcnt vmcnt(0)).  The compiler
+    // does not track which LDS bytes a direct load writes, so this wait is explicit, and
+    // the barrier carries no fence.  Every LDS read of the step has fed its MFMA by then;
+    // the clobbers keep memory accesses, and the scheduling barriers keep all instructions,
+    // on their side of the barrier.
+    auto sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left alone
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    load_b(KB, B0);
+    if constexpr (META == 1) load_m(KB, MM);
+    __builtin_amdgcn_sched_barrier(0);
+    dma(KB, 0);
+    sync();
+    int t = 0;
+    for (; t + 2 <= KT; t += 2) {
+      const int kt = KB + t;
+      load_b(kt + 1, B1);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(kt + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (META == 1) {
+        dc_wide(MM, 0, dcA);
+        dc_wide(MM, 1, dcB);
+      } else if constexpr (META == 2) {
+        dc_step(B0, dcA);
+      }
+      compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
+      sync();
+      load_b(kt + 2, B0);
+      if constexpr (META == 1) load_m(kt + 2, MM);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(kt + 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (META == 2) dc_step(B1, dcB);
+      compute(B1, dcB, reinterpret_cast<const uint16_t*>(lds + BUFB));
+      sync();
+    }
+    if (t < KT) {
+      if constexpr (META == 1) dc_wide(MM, 0, dcA);
+      else if constexpr (META == 2) dc_step(B0, dcA);
+      compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
+    }
+  } else {
   load_b(KB, B0);
   if constexpr (META == 1) load_m(KB, MM);
   load_a(KB, A0);
@@ -271,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     else if constexpr (META == 2) dc_step(B0, dcA);
     compute(B0, dcA, As0);
   }
+  }
 
   // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
   // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][N] plane,
@@ -302,11 +383,11 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 }
 
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA>
 hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16>;
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA>;
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
-  const int lds = 2 * BM * kLR * 2;
+  const int lds = DMA ? 2 * BM * 128 : 2 * BM * kLR * 2;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -325,29 +406,31 @@ hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) 
   return launch_splitk_reduce(part, splits, a.M, a.N, a.ep, st);
 }
 
-template <int FM, int FN, bool KTAIL, bool F16>
+template <int FM, int FN, bool KTAIL, bool F16, bool DMA>
 hipError_t launch_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16>(a, splits, part, st);
+  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16, DMA>(a, splits, part, st);
   const bool g16 = a.group == 16;
   if (a.K % 128 == 0) {
     switch (a.group) {
-      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16>(a, splits, part, st);
-      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16>(a, splits, part, st);
-      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16>(a, splits, part, st);
-      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16>(a, splits, part, st);
+      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16, DMA>(a, splits, part, st);
+      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, splits, part, st);
+      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, splits, part, st);
+      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, splits, part, st);
     }
   }
-  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16>(a, splits, part, st)
-             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16>(a, splits, part, st);
+  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16, DMA>(a, splits, part, st)
+             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16, DMA>(a, splits, part, st);
 }
 
 template <int FM, int FN>
 hipError_t launch_tile(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  if (a.a_f16)
-    return a.K % kBK == 0 ? launch_meta<FM, FN, false, true>(a, splits, part, st)
-                          : launch_meta<FM, FN, true, true>(a, splits, part, st);
-  return a.K % kBK == 0 ? launch_meta<FM, FN, false, false>(a, splits, part, st)
-                        : launch_meta<FM, FN, true, false>(a, splits, part, st);
+  // K % 64 == 0: direct LDS loads of the activation tile; otherwise the register path,
+  // which zeroes the activation columns past K
+  if (a.K % kBK != 0)
+    return a.a_f16 ? launch_meta<FM, FN, true, true, false>(a, splits, part, st)
+                   : launch_meta<FM, FN, true, false, false>(a, splits, part, st);
+  return a.a_f16 ? launch_meta<FM, FN, false, true, true>(a, splits, part, st)
+                 : launch_meta<FM, FN, false, false, true>(a, splits, part, st);
 }
 
 }  // namespace
