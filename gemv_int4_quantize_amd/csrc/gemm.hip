@@ -37,6 +37,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdio>
 #include <cstdlib>
 
@@ -59,7 +60,9 @@ constexpr int lds_row() { return BK + 8; }
 // STAGES: 2 (loads of step k+1 in flight during step k), 3 (loads of step k+2), or 4 (two LDS
 // stages, loads of step k+2, stores of step k+1 interleaved with the MFMAs of step k).
 // F16: fp16 activations and weight operand (v_mfma_f32_32x32x16_f16), else bf16.
-template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES, bool F16>
+// DMA (transposed, STAGES = 4, N % BK == 0): the dY tile goes global -> LDS with direct
+// loads instead of through the staging registers.
+template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int META, int MPT, int STAGES, bool F16, bool DMA>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __restrict__ A,
                                                             const int32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
@@ -78,9 +81,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   static_assert(W_PER_T >= 1 && W_PER_T <= 8 && BN * SLOTS % T == 0, "weight tile split");
 
   constexpr int LST = STAGES == 4 ? 2 : STAGES;  // LDS stages (4: two, interleaved stores)
+  static_assert(!DMA || (TRANS && STAGES == 4), "direct activation loads: interleaved transposed tiles");
+  // activation rows: padded by 16 bytes, or (DMA) unpadded with the 16-byte chunk index
+  // XOR-ed by (row >> ASH) % SLOTS, which keeps the 32 rows of a fragment read in
+  // distinct banks (a direct load writes 64 consecutive 16-byte slots, so rows cannot
+  // be padded)
+  constexpr int LRA = DMA ? BK : LR;
+  constexpr int ASH = SLOTS == 8 ? 2 : SLOTS == 4 ? 3 : 4;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* As = smem;                          // [LST][BM][LR]
-  uint16_t* Bs = smem + LST * BM * LR;          // [LST][BN][LR]
+  uint16_t* As = smem;                          // [LST][BM][LRA]
+  uint16_t* Bs = smem + LST * BM * LRA;         // [LST][BN][LR]
   // Transposed mode: the weight tile is written column-wise (rows 8 apart per lane), which
   // puts the lanes of one LDS write in the same banks; XOR-ing the 16-byte chunk index of
   // row k with (k / 16) spreads them while the 16 consecutive rows of an MFMA operand read
@@ -110,6 +120,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     u32x4 a[A_UNITS];
     uint32_t w[W_PER_T];
     uint16_t s[W_PER_T], z[W_PER_T];
+    uint32_t sv[4], zv[4];  // transposed rowwise: the W_PER_T rows' pairs as loaded
+  };
+  // scale / zero bits of staged row i: transposed rowwise ones are split out of the loaded
+  // words only where they are used, so the loads do not have to land when issued
+  auto s_of = [](const Regs& R, int i) -> uint16_t {
+    if constexpr (TRANS && META == META_ROW) return (uint16_t)(R.sv[i / 2] >> (16 * (i & 1)));
+    else return R.s[i];
+  };
+  auto z_of = [](const Regs& R, int i) -> uint16_t {
+    if constexpr (TRANS && META == META_ROW) return (uint16_t)(R.zv[i / 2] >> (16 * (i & 1)));
+    else return R.z[i];
   };
 
   auto meta_index = [&](int n, int wcol) -> size_t {
@@ -134,7 +155,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
       const int u = tid + i * T;
-      t_aoff[i] = ((uint32_t)(u / SLOTS) * (uint32_t)L + (uint32_t)(u % SLOTS) * 8u) * 2u;
+      const int row = u / SLOTS;
+      const int ch = DMA ? ((u % SLOTS) ^ ((row >> ASH) & (SLOTS - 1))) : u % SLOTS;
+      t_aoff[i] = ((uint32_t)row * (uint32_t)L + (uint32_t)ch * 8u) * 2u;
     }
     const int wc = tid % WCOLS, rb = tid / WCOLS;
     const int wcol = min((c0 >> 3) + wc, KW - 1);
@@ -153,9 +176,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   auto load_stage = [&](int kt, Regs& R) {
     const int l0 = (KB + kt) * BK;
     if constexpr (TRANS) {
+      if constexpr (!DMA) {
 #pragma unroll
-      for (int i = 0; i < A_UNITS; ++i)
-        R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t_ar, t_aoff[i] + (uint32_t)l0 * 2, 0, 0));
+        for (int i = 0; i < A_UNITS; ++i)
+          R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(t_ar, t_aoff[i] + (uint32_t)l0 * 2, 0, 0));
+      }
       // uniform values, kept in scalar registers (a vector min / max here would make the
       // resource descriptor per-lane and every load a waterfall loop)
       const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BK, N - l0)));
@@ -176,7 +201,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
         // the W_PER_T consecutive rows' pairs in one load per array
         const rsrc_t sr = make_rsrc(scales + nb, (uint32_t)(rows * 2));
         const rsrc_t zr = make_rsrc(zeros + nb, (uint32_t)(rows * 2));
-        uint32_t sv[4] = {}, zv[4] = {};
+        uint32_t* sv = R.sv;
+        uint32_t* zv = R.zv;
         if constexpr (W_PER_T == 8) {
           const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, t_moff, 0, 0));
           const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, t_moff, 0, 0));
@@ -192,11 +218,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
         } else {
           sv[0] = __builtin_amdgcn_raw_buffer_load_b16(sr, t_moff, 0, 0);
           zv[0] = __builtin_amdgcn_raw_buffer_load_b16(zr, t_moff, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < W_PER_T; ++i) {
-          R.s[i] = (uint16_t)(sv[i / 2] >> (16 * (i & 1)));
-          R.z[i] = (uint16_t)(zv[i / 2] >> (16 * (i & 1)));
         }
       } else {
 #pragma unroll
@@ -259,14 +280,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   };
 
   auto store_stage = [&](int kt, const Regs& R, int buf) {
-    uint16_t* as = As + buf * BM * LR;
+    uint16_t* as = As + buf * BM * LRA;
     uint16_t* bs = Bs + buf * BN * LR;
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int i = 0; i < A_UNITS; ++i) {
-      const int u = tid + i * T;
-      const int row = u / SLOTS, slot = u % SLOTS;
-      const bool in = TRANS ? (KB + kt) * BK + slot * 8 < L : true;
-      *reinterpret_cast<u32x4*>(as + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < A_UNITS; ++i) {
+        const int u = tid + i * T;
+        const int row = u / SLOTS, slot = u % SLOTS;
+        const bool in = TRANS ? (KB + kt) * BK + slot * 8 < L : true;
+        *reinterpret_cast<u32x4*>(as + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     if constexpr (!TRANS) {
       constexpr int TPR = SLOTS / W_PER_T;
@@ -292,8 +315,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int i1 = 2 * p + 1 < W_PER_T ? 2 * p + 1 : 2 * p;
-        dq_rows_op<F16>(R.w[2 * p], dq_const_mix(R.s[2 * p], R.z[2 * p]), R.w[i1], dq_const_mix(R.s[i1], R.z[i1]),
-                        pk[p]);
+        dq_rows_op<F16>(R.w[2 * p], dq_const_mix(s_of(R, 2 * p), z_of(R, 2 * p)), R.w[i1],
+                        dq_const_mix(s_of(R, i1), z_of(R, i1)), pk[p]);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -323,14 +346,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   // contraction slots 8 (l / 32) .. +7 of the 16-wide step
   const int lr = lane & 31;
   const int lk = (lane >> 5) * 8;
+  // activation fragment: row (wm FM + i) 32 + lr, contraction chunk 2 kk + lane / 32
+  auto a_frag = [&](const uint16_t* abuf, int i, int kk) -> u32x4 {
+    if constexpr (DMA) {
+      const int ch = (2 * kk + (lane >> 5)) ^ ((lr >> ASH) & (SLOTS - 1));
+      return *reinterpret_cast<const u32x4*>(abuf + (wm * FM * 32 + i * 32 + lr) * LRA + ch * 8);
+    } else {
+      return *reinterpret_cast<const u32x4*>(abuf + (wm * FM * 32 + lr) * LR + lk + i * 32 * LR + kk * 16);
+    }
+  };
   auto compute = [&](int buf) {
-    const uint16_t* as = As + buf * BM * LR + (wm * FM * 32 + lr) * LR + lk;
+    const uint16_t* abuf = As + buf * BM * LRA;
     const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       u32x4 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * LR + kk * 16);
+      for (int i = 0; i < FM; ++i) af[i] = a_frag(abuf, i, kk);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         bfr[j] = *reinterpret_cast<const u32x4*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
@@ -351,9 +383,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     if constexpr (STAGES == 4) {
     constexpr int KK = BK / 16;
     constexpr int AU_PER = (A_UNITS + KK - 1) / KK;
-    const uint16_t* as = As + buf * BM * LR + (wm * FM * 32 + lr) * LR + lk;
+    const uint16_t* abuf = As + buf * BM * LRA;
     const uint16_t* bs = Bs + buf * BN * LR + (wn * FN * 32 + lr) * LR;
-    uint16_t* asw = As + sbuf * BM * LR;
+    uint16_t* asw = As + sbuf * BM * LRA;
     uint16_t* bsw = Bs + sbuf * BN * LR;
     constexpr int WCOLS = BN / 8;
     const int wc = tid % WCOLS;
@@ -363,7 +395,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + i * 32 * LR + kk * 16);
+      for (int i = 0; i < FM; ++i) af[i] = a_frag(abuf, i, kk);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         bfr[j] = *reinterpret_cast<const u32x4*>(bs + j * 32 * LR + bswz(wn * FN * 32 + j * 32 + lr, kk * 16 + lk));
@@ -375,7 +407,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 #pragma unroll
       for (int q = 0; q < AU_PER; ++q) {
         const int i = kk * AU_PER + q;
-        if (i < A_UNITS) {
+        if (!DMA && i < A_UNITS) {
           const int u = tid + i * T;
           const int row = u / SLOTS, slot = u % SLOTS;
           const bool in = (KB + kt_s) * BK + slot * 8 < L;
@@ -386,8 +418,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       for (int pp = 0; pp < W_PER_T / 2; ++pp) {
         const int i = 2 * pp;  // rows i, i + 1 of the word column, in slice pp * KK / pairs
         if (pp * KK / (W_PER_T / 2) == kk)
-          dq_rows_op<F16>(R.w[i], dq_const_mix(R.s[i], R.z[i]), R.w[i + 1], dq_const_mix(R.s[i + 1], R.z[i + 1]),
-                          pk[i / 2]);
+          dq_rows_op<F16>(R.w[i], dq_const_mix(s_of(R, i), z_of(R, i)), R.w[i + 1],
+                          dq_const_mix(s_of(R, i + 1), z_of(R, i + 1)), pk[i / 2]);
       }
     }
 #pragma unroll
@@ -400,7 +432,61 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     }
   };
 
-  if constexpr (STAGES == 4) {
+  if constexpr (DMA) {
+    // As STAGES == 4 below, with the dY tile of step k + 1 loaded straight into LDS during
+    // step k.  Each step issues the direct tile loads and then the weight loads of step
+    // k + 2; vector-memory loads complete in issue order, so waiting until only the NW
+    // weight loads of the step are outstanding means the tile has landed, while those
+    // weights keep two steps to arrive.  The barrier carries no fence (a workgroup fence
+    // would wait for every load in flight), so the wait also covers the LDS stores.
+    constexpr int NW = W_PER_T + (META == META_GROUP ? 2 * W_PER_T : META == META_ROW ? 2 : 0);
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto dma_a = [&](int kt, int buf) {
+      const uint32_t l0 = (uint32_t)((KB + kt) * BK);
+      char* base = reinterpret_cast<char*>(As + buf * BM * LRA);
+#pragma unroll
+      for (int i = 0; i < A_UNITS; ++i)
+        // the whole offset in the range-checked vector offset (rows past M read zero); an
+        // int argument, since with an unsigned one the host pass drops the launch stub
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t_ar, (lds_void*)(base + (i * T + wave * 64) * 16), 16,
+                                                 (int)(t_aoff[i] + l0 * 2u), 0, 0, 0);
+    };
+    // s_waitcnt vmcnt(n) lgkmcnt(0), then a barrier with no fence; the clobbers keep memory
+    // accesses, and the scheduling barriers all instructions, on their side of it
+    auto sync = [&](auto n_tag) {
+      constexpr int n = decltype(n_tag)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | ((n >> 4) << 14));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    Regs R0, R1;
+    dma_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(0, R0);
+    load_stage(min(1, KT - 1), R1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage(0, R0, 0);
+    sync(std::integral_constant<int, 0>());
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      dma_a(kt + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(kt + 2, R0);
+      compute_store(0, R1, kt + 1, 1);
+      sync(std::integral_constant<int, NW>());
+      dma_a(kt + 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(kt + 3, R1);
+      compute_store(1, R0, kt + 2, 0);
+      sync(std::integral_constant<int, NW>());
+    }
+    if (kt < KT) compute(0);
+    // no direct LDS load may land after the workgroup's LDS is handed on
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  } else if constexpr (STAGES == 4) {
     // Two LDS stages and two register stages: the loads of step k + 2 are issued before
     // the MFMAs of step k, and step k + 1 (staged during step k - 1) is dequantized and
     // stored in slices between the MFMAs of step k.  Loads past the contraction read
@@ -626,9 +712,14 @@ hipError_t run_k(const MmArgs& a, int splits, float* part, hipStream_t st) {
   constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
   // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
   const bool one = TRANS || META != META_GROUP || a.group >= 8 * WPT;
-  auto k = one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES, F16>
-               : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES, F16>;
-  const size_t lds = (size_t)(STAGES == 4 ? 2 : STAGES) * (BM + BN) * (BK + 8) * 2;
+  // transposed interleaved tiles with N % BK == 0 load the dY tile straight into LDS (no
+  // activation columns past N to zero)
+  constexpr bool DMA_OK = TRANS && STAGES == 4;
+  const bool dma = DMA_OK && a.N % BK == 0;
+  auto k = dma   ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES, F16, DMA_OK>
+           : one ? gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, 1, STAGES, F16, false>
+                 : gemm_kernel<TRANS, WM, WN, FM, FN, BK, META, WPT, STAGES, F16, false>;
+  const size_t lds = (size_t)(STAGES == 4 ? 2 : STAGES) * (BM * (dma ? BK : BK + 8) + BN * (BK + 8)) * 2;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(lds + buf * BUFB + (i * 256 + wave * 64) * 16), 16,
                                                  (int)(a_off[i] + kt * kBK * 2), 0, 0, 0);
     };
-    // Barrier once every load of this wave has landed (s_waitcnt vmcnt(0)).  The compiler
+    // Barrier once every load of this wave has landed (s_waitcnt vmcnt(0) lgkmcnt(0)).  The compiler
     // does not track which LDS bytes a direct load writes, so this wait is explicit, and
     // the barrier carries no fence.  Every LDS read of the step has fed its MFMA by then;
     // the clobbers keep memory accesses, and the scheduling barriers keep all instructions,
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     auto sync = [&]() {
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt left alone
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
