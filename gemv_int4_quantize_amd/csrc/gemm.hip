@@ -626,10 +626,10 @@ struct Cfg {
   float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 0.97f},
+    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 0.9f},
     {0, 4, 2, 2, 2, 64, 4, "gemm_t_256x128", true, 1, 1, 1.0f},
     {0, 2, 2, 2, 2, 32, 4, "gemm_t_128x128", true, 3, 2, 0.65f},
-    {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 1.0f},
+    {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 0.92f},
     {2, 1, 4, 8, 1, 64, 2, "gemm_nt_256x128", false, 2, 2, 1.0f},
     {0, 2, 2, 4, 4, 64, 2, "gemm_nt_lds_256x256", false, 1, 1, 0.7f},
     // short-M tiles (5 <= M < 128): fewer rows per tile waste less of it; the dequantization
