@@ -25,6 +25,7 @@ def _special_weight(N, K, seed):
     w[3, :] = -np.abs(w[3, :]) - 0.1    # all negative
     w[4, 5] = 3.0                       # outliers
     w[5, 17] = -2.5
+    w[6, :] += 100.0                    # narrow range far from 0: zero points near -1e4
     return w
 
 
@@ -130,3 +131,54 @@ def test_quantize_into_row_slices_matches_separate():
         assert_quant_equal(qw, *ref, what=f"fused {mode}")
     with pytest.raises(ValueError):
         w4.quantize_fused([dev_weight(p, "bf16") for p in parts], "global", None)
+
+
+def _tie_weight(N, K, g, dtype, seed):
+    """Groups whose every interior value lands exactly on a rounding tie: with
+    c = m 2^e (m odd, few significant bits, so every value below is exact in the dtype),
+    the group holds lo = -u c and hi = (15 - u) c, so s = c and z = u exactly, and the other
+    values are (k + 1/2 - u) c (u an integer: w / s + z = k + 1/2) or (k - u + 1/2) c with
+    u = v + 1/2 (z fractional, w / s an integer, w / s + z = k + 1/2 again)."""
+    r = np.random.default_rng(seed)
+    mmax = 7 if dtype == "bf16" else 63
+    w = np.empty((N, K), dtype=np.float32)
+    for n in range(N):
+        for g0 in range(0, K, g):
+            c = float(r.choice(np.arange(3, mmax + 1, 2))) * 2.0 ** int(r.integers(-12, -5))
+            if r.integers(2):
+                u = float(r.integers(0, 8))                 # integer zero
+                vals = (np.arange(14) + 0.5 - u) * c
+            else:
+                u = float(r.integers(0, 7)) + 0.5           # fractional zero
+                vals = (np.arange(14) - u + 0.5) * c
+            grp = np.resize(vals, g)
+            grp[:2] = (-u * c, (15.0 - u) * c)
+            w[n, g0:g0 + g] = r.permutation(grp)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode,g,zero", [("groupwise", 16, "fp16"), ("groupwise", 128, "fp16"),
+                                         ("rowwise", None, "fp16"), ("groupwise", 32, "int"),
+                                         ("rowwise", None, "int")])
+def test_quantize_exact_ties(dtype, mode, g, zero):
+    """Every code decided by a tie (w / s + z exactly k + 1/2, or w / s exactly k + 1/2 for
+    integer zeros): the kernel must take the correctly rounded, half-to-even decision."""
+    print(f"[case] quantize ties dtype={dtype} mode={mode} g={g} zero={zero}", flush=True)
+    N, K = 24, 2048
+    w = _tie_weight(N, K, g or K, dtype, 31)
+    if dtype == "f16":
+        w = w.astype(np.float16)
+    elif dtype == "bf16":
+        w = synth.f32_to_bf16_bits(w)
+    w32 = O.to_f32(w, dtype)
+    ref = O.quantize_pack(w32, OMODE[mode], g, int_zero=zero == "int")
+    # the construction does produce ties in the oracle's own arithmetic
+    q, s16, z16 = O.quantize(w32, OMODE[mode], g, int_zero=zero == "int")
+    s_f = np.repeat(s16.astype(np.float32), g or K, axis=1)
+    z_f = np.repeat(z16.astype(np.float32), g or K, axis=1)
+    t = w32 / s_f if zero == "int" else w32 / s_f + z_f
+    assert np.mean(t - np.floor(t) == 0.5) > 0.4
+    qw = w4.quantize_pack(dev_weight(w, dtype), mode, g, zero=zero)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"ties {dtype} {mode} {g} {zero}")
