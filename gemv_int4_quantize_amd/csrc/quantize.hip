@@ -115,40 +115,56 @@ __device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p, bo
   return even | (odd << 4);
 }
 
-// Groups of T * 8 elements (T lanes, T | 64, one word per lane).  Groups tile the
-// rows exactly, so group index = global word index / T.
-template <int DT, int T>
+// Groups of T * WPL words (T lanes, T | 64, WPL consecutive words per lane: 2, or 4 / 8
+// for groups of 256 / 512 words, which a wave then holds in registers).  Two words per lane
+// halve the per-element share of the reduction and of the scale / zero arithmetic, and at
+// g = 16 a lane holds a whole group.  Groups tile the rows exactly, so group index =
+// global lane index / T.
+template <int DT, int T, int WPL>
 __global__ __launch_bounds__(256) void quant_small_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
                                                           uint16_t* __restrict__ scales,
-                                                          uint16_t* __restrict__ zeros, int64_t total_words,
+                                                          uint16_t* __restrict__ zeros, int64_t total_lanes,
                                                           int intz) {
-  const int64_t gw = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = gw < total_words;
-  float v[8];
-  if (valid) {
-    load8<DT>(W, gw * 8, v);
-  } else {
+  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = gl < total_lanes;
+  float v[WPL][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-  }
-  float lo = v[0], hi = v[0];
+  for (int u = 0; u < WPL; ++u) {
+    if (valid) {
+      load8<DT>(W, (gl * WPL + u) * 8, v[u]);
+    } else {
 #pragma unroll
-  for (int j = 1; j < 8; ++j) {
-    lo = __builtin_fminf(lo, v[j]);
-    hi = __builtin_fmaxf(hi, v[j]);
+      for (int j = 0; j < 8; ++j) v[u][j] = 0.0f;
+    }
   }
+  float lo = v[0][0], hi = v[0][0];
+#pragma unroll
+  for (int u = 0; u < WPL; ++u)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo = __builtin_fminf(lo, v[u][j]);
+      hi = __builtin_fmaxf(hi, v[u][j]);
+    }
 #pragma unroll
   for (int o = T / 2; o >= 1; o >>= 1) {
     lo = __builtin_fminf(lo, __shfl_xor(lo, o));
     hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
   }
   const QParams p = qparams(lo, hi, intz != 0);
-  const uint32_t word = pack8(v, p, intz != 0);
+  uint32_t word[WPL];
+#pragma unroll
+  for (int u = 0; u < WPL; ++u) word[u] = pack8(v[u], p, intz != 0);
   if (valid) {
-    packed[gw] = (int32_t)word;
+    if constexpr (WPL == 2) {
+      reinterpret_cast<u32x2*>(packed)[gl] = u32x2{word[0], word[1]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < WPL; u += 4)
+        reinterpret_cast<u32x4*>(packed)[gl * (WPL / 4) + u / 4] = u32x4{word[u], word[u + 1], word[u + 2], word[u + 3]};
+    }
     if ((threadIdx.x & (T - 1)) == 0) {
-      scales[gw / T] = p.sb;
-      zeros[gw / T] = p.zb;
+      scales[gl / T] = p.sb;
+      zeros[gl / T] = p.zb;
     }
   }
 }
@@ -303,17 +319,24 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
 
 // ---------------------------------------------------------------- launchers
 
-template <int DT>
+template <int DT, int WPL>
 static hipError_t quant_small_dispatch(int T, const void* W, int32_t* packed, uint16_t* scales, uint16_t* zeros,
                                        int64_t total_words, int intz, hipStream_t st) {
-  const dim3 grid((unsigned)((total_words + 255) / 256)), block(256);
+  const int64_t lanes = total_words / WPL;
+  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  if constexpr (WPL > 2) {
+    if (T != 64) return hipErrorInvalidValue;
+    quant_small_kernel<DT, 64, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz);
+    return hipGetLastError();
+  }
   switch (T) {
-    case 2: quant_small_kernel<DT, 2><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
-    case 4: quant_small_kernel<DT, 4><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
-    case 8: quant_small_kernel<DT, 8><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
-    case 16: quant_small_kernel<DT, 16><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
-    case 32: quant_small_kernel<DT, 32><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
-    case 64: quant_small_kernel<DT, 64><<<grid, block, 0, st>>>(W, packed, scales, zeros, total_words, intz); break;
+    case 1: quant_small_kernel<DT, 1, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 2: quant_small_kernel<DT, 2, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 4: quant_small_kernel<DT, 4, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 8: quant_small_kernel<DT, 8, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 16: quant_small_kernel<DT, 16, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 32: quant_small_kernel<DT, 32, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
+    case 64: quant_small_kernel<DT, 64, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -337,8 +360,11 @@ static hipError_t quantize_dt(const void* W, int64_t N, int64_t K, int mode, int
   }
   const int64_t gsize = mode == W4_MODE_ROWWISE ? K : g;
   const int64_t wpg = gsize / 8;
-  if (wpg <= 64 && (wpg & (wpg - 1)) == 0 && wpg >= 2)
-    return quant_small_dispatch<DT>((int)wpg, W, packed, scales, zeros, total_words, intz, st);
+  // power-of-two groups of up to 512 words: one pass with the group in registers
+  if (wpg <= 128 && (wpg & (wpg - 1)) == 0 && wpg >= 2)
+    return quant_small_dispatch<DT, 2>((int)(wpg / 2), W, packed, scales, zeros, total_words, intz, st);
+  if (wpg == 256) return quant_small_dispatch<DT, 4>(64, W, packed, scales, zeros, total_words, intz, st);
+  if (wpg == 512) return quant_small_dispatch<DT, 8>(64, W, packed, scales, zeros, total_words, intz, st);
   const int64_t ngroups = total_words / wpg;
   quant_large_kernel<DT><<<(unsigned)((ngroups + 3) / 4), 256, 0, st>>>(W, packed, scales, zeros, ngroups, (int)wpg,
                                                                          intz);
