@@ -69,7 +69,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ zeros,
                                                             const Epi ep,
                                                             int M, int N, int K, int log2g, int kt_per_slice,
-                                                            float* __restrict__ part) {
+                                                            int ct0, int pw, float* __restrict__ part) {
   constexpr int T = WM * WN * 64;
   constexpr int BM = WM * FM * 32;
   constexpr int BN = WN * FN * 32;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = blockIdx.y * BM;
-  const int c0 = blockIdx.x * BN;
+  const int c0 = (blockIdx.x + ct0) * BN;
   // contraction steps of this workgroup: all of them, or one slice of a split-K launch
   const int KT_ALL = (L + BK - 1) / BK;
   const int KB = blockIdx.z * kt_per_slice;
@@ -564,7 +564,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 
   // ---- epilogue.  Result register r of a 32x32 block sits at row 8 (r / 4) +
   // 4 (lane / 32) + (r % 4), column lane % 32.  A split-K slice writes its partial sums
-  // (fp32, no bias) to its own [M][OUTC] plane of `part`; an unsplit launch stores
+  // (fp32, no bias) to its own [M][pw] plane of `part`; an unsplit launch stores
   // through the output epilogue (bias, output dtype, output segments).
   const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
   const int cbase = c0 + wn * FN * 32 + lr;
@@ -573,13 +573,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
     const int c = cbase + j * 32;
     if (c >= OUTC) continue;
     if (part != nullptr) {
-      float* out = part + (size_t)blockIdx.z * M * OUTC;
+      float* out = part + (size_t)blockIdx.z * M * pw;
+      const int pc = c - ct0 * BN;  // column within the plane
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (m < M) out[(size_t)m * OUTC + c] = acc[i][j][r];
+          if (m < M) out[(size_t)m * pw + pc] = acc[i][j][r];
         }
     } else {
       const EpiCol col = epi_col(ep, c);
@@ -594,16 +595,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   }
 }
 
-// Split-K reduction: output = epilogue(sum over the S partial [M][outc] planes, in a
-// fixed order).
+// Split-K reduction: output columns [c_lo, c_lo + pw) = epilogue(sum over the S partial
+// [M][pw] planes, in a fixed order).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
-                                                            int64_t outc, const Epi ep) {
-  const int64_t total = M * outc;
+                                                            int64_t c_lo, int64_t pw, const Epi ep) {
+  const int64_t total = M * pw;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     float v = part[i];
     for (int s = 1; s < S; ++s) v += part[(size_t)s * total + i];
-    const int64_t m = i / outc, c = i - m * outc;
-    epi_put(ep, epi_col(ep, c), m, v);
+    const int64_t m = i / pw, c = i - m * pw;
+    epi_put(ep, epi_col(ep, c_lo + c), m, v);
   }
 }
 
@@ -641,9 +642,14 @@ constexpr Cfg kCfgs[] = {
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
 
+// splits > 1: every tile's contraction is split.  tail_cols > 0: the first column tiles
+// (a whole number of rounds of workgroups) run unsplit and the last tail_cols column tiles
+// run with their contraction split tail_splits ways, so the last, partial round of an
+// unsplit launch becomes short slices spread over every CU.
 struct Plan {
   int cfg;
   int splits;
+  int tail_cols = 0, tail_splits = 1;
 };
 
 // Choose the tile configuration and the split-K factor: score = full-tile efficiency x
@@ -689,6 +695,27 @@ Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
         best_score = score;
         best = Plan{i, sp};
       }
+      // split tail: whole tile columns that fill the full rounds run unsplit, the rest split
+      if (sp == 1 && allow_split && wgs > resident && wgs % resident != 0) {
+        const int64_t main_cols = wgs / resident * resident / tm;
+        const int64_t tail_cols = tn - main_cols;
+        if (main_cols > 0 && tail_cols > 0) {
+          const int64_t main_rounds = (main_cols * tm + resident - 1) / resident;
+          for (int ts = 2; ts <= 8; ts *= 2) {
+            if (kt / ts < 16) break;
+            const float tail_rounds = (float)((tail_cols * tm * ts + resident - 1) / resident) / (float)ts;
+            const float u = (float)wgs / ((float)resident * ((float)main_rounds + tail_rounds));
+            // the tail's partial planes, at twice the whole-split rate: measured, a tail also
+            // pays a second launch and its reduction does not overlap the main launch
+            const float o = (float)tail_cols / (float)tn * 960.0f * (float)ts / (float)L;
+            const float sc = c.eff * u * edge / (1.0f + o);
+            if (sc > best_score) {
+              best_score = sc;
+              best = Plan{i, 1, (int)tail_cols, ts};
+            }
+          }
+        }
+      }
     }
   }
   return best;
@@ -696,7 +723,15 @@ Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
 
 size_t split_bytes(const MmArgs& a, const Plan& p) {
   const int64_t outc = a.transposed ? a.K : a.N;
-  return p.splits > 1 ? (size_t)p.splits * a.M * outc * sizeof(float) : 0;
+  if (p.splits > 1) return (size_t)p.splits * a.M * outc * sizeof(float);
+  if (p.tail_cols > 0) {
+    const Cfg& c = kCfgs[p.cfg];
+    const int64_t bn = c.wn * c.fn * 32;
+    const int64_t tn = (outc + bn - 1) / bn;
+    const int64_t pw = outc - (tn - p.tail_cols) * bn;
+    return (size_t)p.tail_splits * a.M * pw * sizeof(float);
+  }
+  return 0;
 }
 
 int meta_kind(int mode) { return mode == W4_MODE_GLOBAL ? META_GLOBAL : mode == W4_MODE_ROWWISE ? META_ROW : META_GROUP; }
@@ -707,7 +742,7 @@ size_t lds_bytes(const Cfg& c) {
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META, bool F16>
-hipError_t run_k(const MmArgs& a, int splits, float* part, hipStream_t st) {
+hipError_t run_k(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
   constexpr int BM = WM * FM * 32, BN = WN * FN * 32;
   constexpr int WPT = BN * (BK / 8) / (WM * WN * 64);  // packed words per thread per stage
   // one scale / zero pair per thread when its WPT words (8 * WPT codes, aligned) share a group
@@ -728,56 +763,71 @@ hipError_t run_k(const MmArgs& a, int splits, float* part, hipStream_t st) {
   const int64_t outc = TRANS ? a.K : a.N;
   const int64_t L = TRANS ? a.N : a.K;
   const int kt_all = (int)((L + BK - 1) / BK);
+  int splits = gp.splits;
   const int kts = (kt_all + splits - 1) / splits;
   splits = (kt_all + kts - 1) / kts;  // every slice gets at least one contraction step
-  const dim3 grid((unsigned)((outc + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
+  const int tn_all = (int)((outc + BN - 1) / BN);
+  const int nct = gp.nct > 0 ? gp.nct : tn_all - gp.ct0;
+  const int64_t c_lo = (int64_t)gp.ct0 * BN;
+  const int pw = (int)(std::min<int64_t>(outc, c_lo + (int64_t)nct * BN) - c_lo);
+  const dim3 grid((unsigned)nct, (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
   const int log2g = 31 - __builtin_clz((unsigned)a.group);
   k<<<grid, WM * WN * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K,
-                                      log2g, kts, splits > 1 ? part : nullptr);
+                                      log2g, kts, gp.ct0, pw, splits > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, a.M, outc, a.ep, st);
+  return launch_splitk_reduce(part, splits, a.M, c_lo, pw, a.ep, st);
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES, int META>
-hipError_t run(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  return a.a_f16 ? run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, true>(a, splits, part, st)
-                 : run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, false>(a, splits, part, st);
+hipError_t run(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
+  return a.a_f16 ? run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, true>(a, gp, part, st)
+                 : run_k<TRANS, WM, WN, FM, FN, BK, STAGES, META, false>(a, gp, part, st);
 }
 
 template <bool TRANS, int WM, int WN, int FM, int FN, int BK, int STAGES>
-hipError_t run_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
+hipError_t run_meta(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
   switch (meta_kind(a.mode)) {
-    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GLOBAL>(a, splits, part, st);
-    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_ROW>(a, splits, part, st);
-    default: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GROUP>(a, splits, part, st);
+    case META_GLOBAL: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GLOBAL>(a, gp, part, st);
+    case META_ROW: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_ROW>(a, gp, part, st);
+    default: return run<TRANS, WM, WN, FM, FN, BK, STAGES, META_GROUP>(a, gp, part, st);
+  }
+}
+
+hipError_t run_cfg(const MmArgs& a, int cfg, const GemmPart& gp, float* part, hipStream_t st) {
+  if (a.transposed) {
+    switch (cfg) {
+      case 0: return run_meta<true, 2, 2, 4, 4, 64, 4>(a, gp, part, st);
+      case 1: return run_meta<true, 4, 2, 2, 2, 64, 4>(a, gp, part, st);
+      case 8: return run_meta<true, 1, 4, 1, 1, 64, 4>(a, gp, part, st);
+      default: return run_meta<true, 2, 2, 2, 2, 32, 4>(a, gp, part, st);
+    }
+  }
+  switch (kCfgs[cfg].kind) {
+    case 1: return launch_gemm_nt_reg(a, 0, gp, part, st);
+    case 2: return launch_gemm_nt_reg(a, 1, gp, part, st);
+    case 3: return launch_gemm_nt_reg(a, 2, gp, part, st);
+    case 4: return launch_gemm_nt_reg(a, 3, gp, part, st);
+    default: return run_meta<false, 2, 2, 4, 4, 64, 2>(a, gp, part, st);
   }
 }
 
 hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st) {
-  if (a.transposed) {
-    switch (p.cfg) {
-      case 0: return run_meta<true, 2, 2, 4, 4, 64, 4>(a, p.splits, part, st);
-      case 1: return run_meta<true, 4, 2, 2, 2, 64, 4>(a, p.splits, part, st);
-      case 8: return run_meta<true, 1, 4, 1, 1, 64, 4>(a, p.splits, part, st);
-      default: return run_meta<true, 2, 2, 2, 2, 32, 4>(a, p.splits, part, st);
-    }
-  }
-  switch (kCfgs[p.cfg].kind) {
-    case 1: return launch_gemm_nt_reg(a, 0, p.splits, part, st);
-    case 2: return launch_gemm_nt_reg(a, 1, p.splits, part, st);
-    case 3: return launch_gemm_nt_reg(a, 2, p.splits, part, st);
-    case 4: return launch_gemm_nt_reg(a, 3, p.splits, part, st);
-    default: return run_meta<false, 2, 2, 4, 4, 64, 2>(a, p.splits, part, st);
-  }
+  if (p.tail_cols == 0) return run_cfg(a, p.cfg, GemmPart{p.splits, 0, 0}, part, st);
+  const Cfg& c = kCfgs[p.cfg];
+  const int64_t bn = c.wn * c.fn * 32;
+  const int tn = (int)(((a.transposed ? a.K : a.N) + bn - 1) / bn);
+  const hipError_t e = run_cfg(a, p.cfg, GemmPart{1, 0, tn - p.tail_cols}, nullptr, st);
+  if (e != hipSuccess) return e;
+  return run_cfg(a, p.cfg, GemmPart{p.tail_splits, tn - p.tail_cols, p.tail_cols}, part, st);
 }
 
 }  // namespace
 
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t outc, const Epi& ep,
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t c_lo, int64_t pw, const Epi& ep,
                                 hipStream_t st) {
-  const int64_t blocks = (M * outc + 255) / 256;
-  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, outc, ep);
+  const int64_t blocks = (M * pw + 255) / 256;
+  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, c_lo, pw, ep);
   return hipGetLastError();
 }
 
@@ -785,6 +835,10 @@ const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspa
   static thread_local char buf[64];
   const Plan p = pick_plan(a, caps, with_workspace);
   const Cfg& c = kCfgs[p.cfg];
+  if (p.tail_cols > 0) {
+    snprintf(buf, sizeof(buf), "%s_tail%d_splitk%d", c.name, p.tail_cols, p.tail_splits);
+    return buf;
+  }
   if (p.splits == 1) return c.name;
   snprintf(buf, sizeof(buf), "%s_splitk%d", c.name, p.splits);
   return buf;
@@ -800,7 +854,7 @@ size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps) {
 
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st) {
   Plan p = pick_plan(a, caps, ws != nullptr);
-  if (p.splits > 1 && split_bytes(a, p) > ws_bytes) p = pick_plan(a, caps, false);
+  if ((p.splits > 1 || p.tail_cols > 0) && split_bytes(a, p) > ws_bytes) p = pick_plan(a, caps, false);
   return run_plan(a, p, static_cast<float*>(ws), st);
 }
 

@@ -33,6 +33,8 @@
 //     4 VALU per MFMA, which the matrix core mostly overlaps;
 //   * split-K: blockIdx.z takes a contiguous range of steps and writes fp32 partial sums
 //     to its own plane; a separate kernel sums the planes in a fixed order.
+#include <algorithm>
+
 #include "common.h"
 #include "epilogue.h"
 #include "launch.h"
@@ -64,7 +66,8 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ zeros,
                                                          const Epi ep,
                                                          int M, int N, int K, int meta_row, int log2g,
-                                                         int kt_per_slice, float* __restrict__ part) {
+                                                         int kt_per_slice, int ct0, int pw,
+                                                         float* __restrict__ part) {
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   constexpr int AU = BM * 8 / 256;  // 16-byte activation units per thread per step
   static_assert(!(DMA && KTAIL), "direct LDS loads cannot zero the columns past K");
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   uint16_t* As1 = smem + BM * kLR;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = blockIdx.y * BM, c0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * BM, c0 = (blockIdx.x + ct0) * BN;
   const int KT_ALL = (K + kBK - 1) / kBK;
   const int KB = blockIdx.z * kt_per_slice;  // first step of this slice (even)
   const int KT = min(KT_ALL - KB, kt_per_slice);
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 
   // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
-  // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][N] plane,
+  // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][pw] plane,
   // an unsplit launch stores through the output epilogue
   const int rbase = m0 + h * 4;
 #pragma unroll
@@ -362,13 +365,14 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     const int c = n0w + j * 32 + lr;
     if (c >= N) continue;
     if (part != nullptr) {
-      float* out = part + (size_t)blockIdx.z * M * N;
+      float* out = part + (size_t)blockIdx.z * M * pw;
+      const int pc = c - ct0 * BN;  // column within the plane
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-          if (m < M) out[(size_t)m * N + c] = acc[i][j][r];
+          if (m < M) out[(size_t)m * pw + pc] = acc[i][j][r];
         }
     } else {
       const EpiCol col = epi_col(ep, c);
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 }
 
 template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA>
-hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) {
+hipError_t launch_cfg(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
   auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA>;
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   const int lds = DMA ? 2 * BM * 128 : 2 * BM * kLR * 2;
@@ -393,44 +397,49 @@ hipError_t launch_cfg(const MmArgs& a, int splits, float* part, hipStream_t st) 
     if (e != hipSuccess) return e;
   }
   const int kt_all = (int)((a.K + kBK - 1) / kBK);
+  int splits = gp.splits;
   int kts = (kt_all + splits - 1) / splits;
   kts += kts & 1;                     // slices start on even steps (wide scale / zero loads)
   splits = (kt_all + kts - 1) / kts;  // every slice gets at least one step
   const int meta_row = a.mode == W4_MODE_GLOBAL ? 0 : a.mode == W4_MODE_ROWWISE ? 1 : (int)(a.K / a.group);
   const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
-  const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
+  const int tn_all = (int)((a.N + BN - 1) / BN);
+  const int nct = gp.nct > 0 ? gp.nct : tn_all - gp.ct0;
+  const int64_t c_lo = (int64_t)gp.ct0 * BN;
+  const int pw = (int)(std::min<int64_t>(a.N, c_lo + (int64_t)nct * BN) - c_lo);
+  const dim3 grid((unsigned)nct, (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
   k<<<grid, 256, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K, meta_row,
-                            log2g, kts, splits > 1 ? part : nullptr);
+                            log2g, kts, gp.ct0, pw, splits > 1 ? part : nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, a.M, a.N, a.ep, st);
+  return launch_splitk_reduce(part, splits, a.M, c_lo, pw, a.ep, st);
 }
 
 template <int FM, int FN, bool KTAIL, bool F16, bool DMA>
-hipError_t launch_meta(const MmArgs& a, int splits, float* part, hipStream_t st) {
-  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16, DMA>(a, splits, part, st);
+hipError_t launch_meta(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
+  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16, DMA>(a, gp, part, st);
   const bool g16 = a.group == 16;
   if (a.K % 128 == 0) {
     switch (a.group) {
-      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16, DMA>(a, splits, part, st);
-      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, splits, part, st);
-      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, splits, part, st);
-      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, splits, part, st);
+      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16, DMA>(a, gp, part, st);
+      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, gp, part, st);
+      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, gp, part, st);
+      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
     }
   }
-  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16, DMA>(a, splits, part, st)
-             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16, DMA>(a, splits, part, st);
+  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16, DMA>(a, gp, part, st)
+             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16, DMA>(a, gp, part, st);
 }
 
 template <int FM, int FN>
-hipError_t launch_tile(const MmArgs& a, int splits, float* part, hipStream_t st) {
+hipError_t launch_tile(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
   // K % 64 == 0: direct LDS loads of the activation tile; otherwise the register path,
   // which zeroes the activation columns past K
   if (a.K % kBK != 0)
-    return a.a_f16 ? launch_meta<FM, FN, true, true, false>(a, splits, part, st)
-                   : launch_meta<FM, FN, true, false, false>(a, splits, part, st);
-  return a.a_f16 ? launch_meta<FM, FN, false, true, true>(a, splits, part, st)
-                 : launch_meta<FM, FN, false, false, true>(a, splits, part, st);
+    return a.a_f16 ? launch_meta<FM, FN, true, true, false>(a, gp, part, st)
+                   : launch_meta<FM, FN, true, false, false>(a, gp, part, st);
+  return a.a_f16 ? launch_meta<FM, FN, false, true, true>(a, gp, part, st)
+                 : launch_meta<FM, FN, false, false, true>(a, gp, part, st);
 }
 
 }  // namespace
@@ -440,12 +449,12 @@ bool gemm_nt_reg_supported(const MmArgs& a) {
   return !a.transposed && a.K <= ((int64_t)1 << 21);
 }
 
-hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st) {
+hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, const GemmPart& gp, float* part, hipStream_t st) {
   switch (tile) {
-    case 0: return launch_tile<4, 1>(a, splits, part, st);  // 128 x 128
-    case 1: return launch_tile<8, 1>(a, splits, part, st);  // 256 x 128
-    case 2: return launch_tile<2, 1>(a, splits, part, st);  // 64 x 128
-    default: return launch_tile<1, 1>(a, splits, part, st);  // 32 x 128
+    case 0: return launch_tile<4, 1>(a, gp, part, st);  // 128 x 128
+    case 1: return launch_tile<8, 1>(a, gp, part, st);  // 256 x 128
+    case 2: return launch_tile<2, 1>(a, gp, part, st);  // 64 x 128
+    default: return launch_tile<1, 1>(a, gp, part, st);  // 32 x 128
   }
 }
 

@@ -65,14 +65,24 @@ size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps);
 size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps);
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st);
 
-// Non-transposed GEMM with the weight operand dequantized into MFMA registers
-// (tile 0: 128 x 128, 1: 256 x 128, 2: 64 x 128, 3: 32 x 128); split-K over `part`
-// when splits > 1.
-bool gemm_nt_reg_supported(const MmArgs& a);
-hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, int splits, float* part, hipStream_t st);
+// The part of a GEMM one launch covers: output column tiles [ct0, ct0 + nct) (nct = 0:
+// all of them from ct0 on), with the contraction cut into `splits` slices.  With
+// splits > 1 each slice writes its fp32 partial sums to its own plane of the workspace,
+// [M][pw] where pw is the number of covered columns (column ct0 * BN first), and a
+// reduction finishes them through the output epilogue.
+struct GemmPart {
+  int splits = 1;
+  int ct0 = 0, nct = 0;
+};
 
-// Output = epilogue(sum of `splits` fp32 [M][outc] planes, in a fixed order).
-hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t outc, const Epi& ep,
+// Non-transposed GEMM with the weight operand dequantized into MFMA registers
+// (tile 0: 128 x 128, 1: 256 x 128, 2: 64 x 128, 3: 32 x 128).
+bool gemm_nt_reg_supported(const MmArgs& a);
+hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, const GemmPart& gp, float* part, hipStream_t st);
+
+// Output columns [c_lo, c_lo + pw) = epilogue(sum of `splits` fp32 [M][pw] planes, in a
+// fixed order).
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t c_lo, int64_t pw, const Epi& ep,
                                 hipStream_t st);
 
 }  // namespace w4

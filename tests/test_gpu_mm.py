@@ -7,7 +7,8 @@ import torch
 import gemv_int4_quantize_amd as w4
 import oracle as O
 import synth
-from gpu_helpers import DEV, assert_mm_close, dev_bf16, dev_f32, dev_weight, host, oracle_rows_global
+from gpu_helpers import (DEV, ELEM_ATOL, ELEM_RTOL, assert_mm_close, dev_bf16, dev_f32, dev_weight, host,
+                         oracle_rows_global)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +191,57 @@ def test_splitk_gemm(ci):
     want = O.matmul(a, *ref, K, t, bias)
     assert_mm_close(host(y1), want, f"splitk {ci}")
     assert_mm_close(host(y0), want, f"unsplit {ci}")
+
+
+TAIL_CASES = [(1536, 2048, 6144, True, "rowwise", None, False), (1536, 11008, 2048, False, "rowwise", None, True),
+              (1024, 2048, 11008, True, "groupwise", 64, True), (1536, 11008, 2048, False, "groupwise", 128, False)]
+
+
+@pytest.mark.parametrize("ci", range(len(TAIL_CASES)),
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}{'t' if c[3] else 'nt'}{c[4]}" for c in TAIL_CASES])
+def test_split_tail_gemm(ci):
+    """A partial last round of workgroups: the whole-round tile columns run unsplit and the
+    rest with a split contraction (compact partial planes, reduction over the tail columns
+    through the epilogue).  Sampled rows match the oracle, with fp32 bias and bf16 output
+    in two cases; results are deterministic; the unsplit launch matches too."""
+    M, N, K, t, mode, g, epi = TAIL_CASES[ci]
+    print(f"[case] split tail M={M} N={N} K={K} t={t} {mode}{g or ''} epi={epi}", flush=True)
+    assert "_tail" in w4.kernel_for(M, N, K, mode, g, transposed=t)
+    w = synth.weight(707, ci, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
+    wdq = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref, K))
+    outc = K if t else N
+    a = synth.activations_bf16(707, ci, M, N if t else K)
+    # bias in the output dtype: bf16 values (as float64 for the oracle)
+    bias = O.bf16_bits_to_f64(O.bf16_rne_bits(synth.bias_f32(707, ci, outc))) if epi else None
+    ad = dev_bf16(a)
+    if epi:
+        bd = torch.from_numpy(bias.astype(np.float32)).to(DEV)
+        kw = dict(transposed=t, bias=bd.to(torch.bfloat16), out_dtype=torch.bfloat16)
+    else:
+        kw = dict(transposed=t)
+    y1 = w4.mm(ad, qw, **kw)
+    y2 = w4.mm(ad, qw, **kw)
+    y0 = w4.mm(ad, qw, split_k=False, **kw)
+    assert torch.equal(y1, y2)
+    if epi:
+        # the bf16 output is the fp32 epilogue value of the same plan, rounded once
+        y32 = w4.mm(ad, qw, transposed=t, bias=bd)
+        assert torch.equal(y1, y32.to(torch.bfloat16))
+    ms = np.sort(np.random.default_rng(ci).choice(M, 16, replace=False))
+    msd = torch.from_numpy(ms).to(DEV)
+    want = O.bf16_bits_to_f64(a[ms]) @ (wdq if t else wdq.T)
+    if epi:
+        want = O.round_output(want + bias, "bf16")
+    for y, what in ((y1, "tail"), (y0, "unsplit")):
+        got = host(y[msd].float()).astype(np.float64)
+        if epi:
+            ulp = np.abs(want) * 2.0**-7
+            bad = np.abs(got - want) > ELEM_RTOL * np.abs(want) + ELEM_ATOL + ulp
+            assert not bad.any(), f"{int(bad.sum())} elements outside the bound, {what} {ci}"
+        else:
+            assert_mm_close(got, want, f"{what} {ci}")
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled outputs
