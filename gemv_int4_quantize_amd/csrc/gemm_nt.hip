@@ -57,9 +57,11 @@ constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
 // META: 0 one (scale, zero) per row (rowwise / global), 1 groupwise with one wide load per
 // two steps, 2 groupwise with one pair per step.  GPW: groups per 32-value lane chunk
 // (2 when g = 16).  KTAIL: K % 64 != 0 (activation columns past K are zeroed in LDS).
-// WB (META 1): bytes of one wide load = 2 max(1, 128 / g), a compile-time width so that the
-// loop holds exactly one load form.
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA>
+// WB (META 1): bytes of one wide load, a compile-time width so that the loop holds exactly
+// one load form; SPL (META 1): the contraction steps one wide load covers (2, or 4 / 8 when
+// K allows: four or eight times fewer scale / zero loads).  One load holds the pairs of
+// SPL * 64 / g consecutive groups, so g = 128 SPL / WB when a group is at most 64 SPL wide.
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL>
 __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   constexpr int AU = BM * 8 / 256;  // 16-byte activation units per thread per step
   static_assert(!(DMA && KTAIL), "direct LDS loads cannot zero the columns past K");
+  static_assert(SPL == 2 || (DMA && META == 1), "wide scale / zero loads over more than two steps: direct path");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* As0 = smem;
   uint16_t* As1 = smem + BM * kLR;
@@ -225,14 +228,17 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
           acc[i][j] = mfma_op<F16>(af[c][i], bfr[c][j], acc[i][j]);
     }
   };
-  // dequantization constants of step p (0: kt, 1: kt + 1) from the wide meta registers:
-  // half index g=16: 4p + 2h + q; g=32: 2p + h; g=64: p; g>=128: 0
+  // dequantization constants of step p of a wide load's SPL steps: this lane's 16 values
+  // (q-th group of them when g = 16) start at column 64 p + 32 h + 16 q of the block, in
+  // group (64 p + 32 h + 16 q) / GW with GW = 128 SPL / WB (g, or 128 for any g >= 128
+  // at SPL = 2, where one pair covers both steps)
   auto dc_wide = [&](const MRegs& R, int p, DqConst (&dc)[FN][GPW]) {
+    constexpr int GW = WB > 0 ? 128 * SPL / WB : 1;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < GPW; ++q) {
-        const int e = GPW == 2 ? 4 * p + 2 * h + q : WB == 8 ? 2 * p + h : WB == 4 ? p : 0;
+        const int e = (64 * p + 32 * h + 16 * q) / GW;
         dc[j][q] = dq_const_mix(half_of(R.s[j], e), half_of(R.z[j], e));
       }
   };
@@ -291,34 +297,70 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
     __builtin_amdgcn_sched_barrier(0);
     dma(KB, 0);
     sync();
-    int t = 0;
-    for (; t + 2 <= KT; t += 2) {
-      const int kt = KB + t;
-      load_b(kt + 1, B1);
+    // step kt = KB + t + p (p-th of a block of SPL steps): loads of step kt + 1, then the
+    // products of step kt from LDS buffer p % 2 and weight registers Bc
+    auto step = [&](BRegs& Bc, BRegs& Bn, int p, int kt) {
+      load_b(kt + 1, Bn);
       __builtin_amdgcn_sched_barrier(0);
-      dma(kt + 1, 1);
+      dma(kt + 1, (p + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (META == 1) {
-        dc_wide(MM, 0, dcA);
-        dc_wide(MM, 1, dcB);
-      } else if constexpr (META == 2) {
-        dc_step(B0, dcA);
+      const uint16_t* buf = reinterpret_cast<const uint16_t*>(lds + (p & 1) * BUFB);
+      if constexpr (META == 0) {
+        compute(Bc, dcA, buf);
+      } else {
+        DqConst dc[FN][GPW];
+        if constexpr (META == 1) {
+          dc_wide(MM, p, dc);
+          if (p == SPL - 1) load_m(kt + 1, MM);  // the next block's pairs, once these are read
+        } else {
+          dc_step(Bc, dc);
+        }
+        compute(Bc, dc, buf);
       }
-      compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
       sync();
-      load_b(kt + 2, B0);
-      if constexpr (META == 1) load_m(kt + 2, MM);
-      __builtin_amdgcn_sched_barrier(0);
-      dma(kt + 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (META == 2) dc_step(B1, dcB);
-      compute(B1, dcB, reinterpret_cast<const uint16_t*>(lds + BUFB));
-      sync();
-    }
-    if (t < KT) {
-      if constexpr (META == 1) dc_wide(MM, 0, dcA);
-      else if constexpr (META == 2) dc_step(B0, dcA);
-      compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
+    };
+    if constexpr (SPL > 2) {
+      // blocks of SPL steps start on multiples of SPL (slices too, and K is a multiple of
+      // SPL steps), so step parity picks the buffers
+      for (int t = 0; t < KT; t += SPL) {
+#pragma unroll
+        for (int p = 0; p < SPL; ++p) {
+          if (p & 1) step(B1, B0, p, KB + t + p);
+          else step(B0, B1, p, KB + t + p);
+        }
+      }
+    } else {
+      // two steps per iteration and a peeled last step (measured faster than the block form
+      // for rowwise and g = 16)
+      int t = 0;
+      for (; t + 2 <= KT; t += 2) {
+        const int kt = KB + t;
+        load_b(kt + 1, B1);
+        __builtin_amdgcn_sched_barrier(0);
+        dma(kt + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (META == 1) {
+          dc_wide(MM, 0, dcA);
+          dc_wide(MM, 1, dcB);
+        } else if constexpr (META == 2) {
+          dc_step(B0, dcA);
+        }
+        compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
+        sync();
+        load_b(kt + 2, B0);
+        if constexpr (META == 1) load_m(kt + 2, MM);
+        __builtin_amdgcn_sched_barrier(0);
+        dma(kt + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (META == 2) dc_step(B1, dcB);
+        compute(B1, dcB, reinterpret_cast<const uint16_t*>(lds + BUFB));
+        sync();
+      }
+      if (t < KT) {
+        if constexpr (META == 1) dc_wide(MM, 0, dcA);
+        else if constexpr (META == 2) dc_step(B0, dcA);
+        compute(B0, dcA, reinterpret_cast<const uint16_t*>(lds));
+      }
     }
   } else {
   load_b(KB, B0);
@@ -387,9 +429,9 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 }
 
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA>
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL = 2>
 hipError_t launch_cfg(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
-  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA>;
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA, SPL>;
   constexpr int BM = FM * 32, BN = 4 * FN * 32;
   const int lds = DMA ? 2 * BM * 128 : 2 * BM * kLR * 2;
   if (lds > 64 * 1024) {
@@ -399,7 +441,7 @@ hipError_t launch_cfg(const MmArgs& a, const GemmPart& gp, float* part, hipStrea
   const int kt_all = (int)((a.K + kBK - 1) / kBK);
   int splits = gp.splits;
   int kts = (kt_all + splits - 1) / splits;
-  kts += kts & 1;                     // slices start on even steps (wide scale / zero loads)
+  kts = (kts + SPL - 1) / SPL * SPL;  // slices start on whole wide scale / zero loads
   splits = (kt_all + kts - 1) / kts;  // every slice gets at least one step
   const int meta_row = a.mode == W4_MODE_GLOBAL ? 0 : a.mode == W4_MODE_ROWWISE ? 1 : (int)(a.K / a.group);
   const int log2g = a.mode == W4_MODE_GROUPWISE ? 31 - __builtin_clz((unsigned)a.group) : 31;
@@ -420,10 +462,23 @@ hipError_t launch_meta(const MmArgs& a, const GemmPart& gp, float* part, hipStre
   if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16, DMA>(a, gp, part, st);
   const bool g16 = a.group == 16;
   if (a.K % 128 == 0) {
+    // direct path: one 16- or 8-byte load covering 4 or 8 steps where K allows
     switch (a.group) {
       case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16, DMA>(a, gp, part, st);
-      case 32: return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, gp, part, st);
-      case 64: return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, gp, part, st);
+      case 32:
+        if constexpr (DMA)
+          if (a.K % 256 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 16, F16, DMA, 4>(a, gp, part, st);
+        return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, gp, part, st);
+      case 64:
+        if constexpr (DMA) {
+          if (a.K % 512 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 16, F16, DMA, 8>(a, gp, part, st);
+          if (a.K % 256 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA, 4>(a, gp, part, st);
+        }
+        return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, gp, part, st);
+      case 128:
+        if constexpr (DMA)
+          if (a.K % 512 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA, 8>(a, gp, part, st);
+        return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
       default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
     }
   }
