@@ -120,52 +120,106 @@ __device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p, bo
 // halve the per-element share of the reduction and of the scale / zero arithmetic, and at
 // g = 16 a lane holds a whole group.  Groups tile the rows exactly, so group index =
 // global lane index / T.
+// One word of W as loaded (8 elements: one 16-byte load, two for fp32), widened to fp32
+// only when used, so the next word's load can be in flight meanwhile.
+template <int DT>
+struct RawWord {
+  u32x4 a, b;
+};
+template <int DT>
+__device__ __forceinline__ void load_raw(const void* W, int64_t off, RawWord<DT>& r) {
+  if constexpr (DT == W4_DT_F32) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(W) + off);
+    r.a = p[0];
+    r.b = p[1];
+  } else {
+    r.a = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + off);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void widen(const RawWord<DT>& r, float v[8]) {
+  if constexpr (DT == W4_DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(r.a[i]);
+      v[4 + i] = __uint_as_float(r.b[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == W4_DT_F16) {
+        v[2 * i] = f16_bits_to_f32(r.a[i] & 0xFFFFu);
+        v[2 * i + 1] = f16_bits_to_f32(r.a[i] >> 16);
+      } else {
+        v[2 * i] = __uint_as_float(r.a[i] << 16);
+        v[2 * i + 1] = __uint_as_float(r.a[i] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
 template <int DT, int T, int WPL>
 __global__ __launch_bounds__(256) void quant_small_kernel(const void* __restrict__ W, int32_t* __restrict__ packed,
                                                           uint16_t* __restrict__ scales,
                                                           uint16_t* __restrict__ zeros, int64_t total_lanes,
                                                           int intz) {
-  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = gl < total_lanes;
-  float v[WPL][8];
+  // grid-stride over blocks of 256 lanes, the next block's words loaded while this one is
+  // quantized; a lane past the end holds zeros (a group's lanes are all in or all out)
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  auto fetch = [&](int64_t base, RawWord<DT> (&r)[WPL]) {
+    const int64_t gl = base + threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < WPL; ++u) {
+    for (int u = 0; u < WPL; ++u) {
+      if (gl < total_lanes) {
+        load_raw<DT>(W, (gl * WPL + u) * 8, r[u]);
+      } else {
+        r[u].a = u32x4{0u, 0u, 0u, 0u};
+        r[u].b = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  RawWord<DT> cur[WPL], nxt[WPL];
+  int64_t base = (int64_t)blockIdx.x * 256;
+  fetch(base, cur);
+  for (; base < total_lanes; base += stride) {
+    fetch(base + stride, nxt);
+    const int64_t gl = base + threadIdx.x;
+    const bool valid = gl < total_lanes;
+    float v[WPL][8];
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) widen<DT>(cur[u], v[u]);
+    float lo = v[0][0], hi = v[0][0];
+#pragma unroll
+    for (int u = 0; u < WPL; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        lo = __builtin_fminf(lo, v[u][j]);
+        hi = __builtin_fmaxf(hi, v[u][j]);
+      }
+#pragma unroll
+    for (int o = T / 2; o >= 1; o >>= 1) {
+      lo = __builtin_fminf(lo, __shfl_xor(lo, o));
+      hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
+    }
+    const QParams p = qparams(lo, hi, intz != 0);
+    uint32_t word[WPL];
+#pragma unroll
+    for (int u = 0; u < WPL; ++u) word[u] = pack8(v[u], p, intz != 0);
     if (valid) {
-      load8<DT>(W, (gl * WPL + u) * 8, v[u]);
-    } else {
+      if constexpr (WPL == 2) {
+        reinterpret_cast<u32x2*>(packed)[gl] = u32x2{word[0], word[1]};
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[u][j] = 0.0f;
-    }
-  }
-  float lo = v[0][0], hi = v[0][0];
-#pragma unroll
-  for (int u = 0; u < WPL; ++u)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo = __builtin_fminf(lo, v[u][j]);
-      hi = __builtin_fmaxf(hi, v[u][j]);
+        for (int u = 0; u < WPL; u += 4)
+          reinterpret_cast<u32x4*>(packed)[gl * (WPL / 4) + u / 4] = u32x4{word[u], word[u + 1], word[u + 2], word[u + 3]};
+      }
+      if ((threadIdx.x & (T - 1)) == 0) {
+        scales[gl / T] = p.sb;
+        zeros[gl / T] = p.zb;
+      }
     }
 #pragma unroll
-  for (int o = T / 2; o >= 1; o >>= 1) {
-    lo = __builtin_fminf(lo, __shfl_xor(lo, o));
-    hi = __builtin_fmaxf(hi, __shfl_xor(hi, o));
-  }
-  const QParams p = qparams(lo, hi, intz != 0);
-  uint32_t word[WPL];
-#pragma unroll
-  for (int u = 0; u < WPL; ++u) word[u] = pack8(v[u], p, intz != 0);
-  if (valid) {
-    if constexpr (WPL == 2) {
-      reinterpret_cast<u32x2*>(packed)[gl] = u32x2{word[0], word[1]};
-    } else {
-#pragma unroll
-      for (int u = 0; u < WPL; u += 4)
-        reinterpret_cast<u32x4*>(packed)[gl * (WPL / 4) + u / 4] = u32x4{word[u], word[u + 1], word[u + 2], word[u + 3]};
-    }
-    if ((threadIdx.x & (T - 1)) == 0) {
-      scales[gl / T] = p.sb;
-      zeros[gl / T] = p.zb;
-    }
+    for (int u = 0; u < WPL; ++u) cur[u] = nxt[u];
   }
 }
 
@@ -319,11 +373,14 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
 
 // ---------------------------------------------------------------- launchers
 
+constexpr int64_t kQuantBlocks = 4096;  // grid of the grid-stride quantize kernel
+
 template <int DT, int WPL>
 static hipError_t quant_small_dispatch(int T, const void* W, int32_t* packed, uint16_t* scales, uint16_t* zeros,
                                        int64_t total_words, int intz, hipStream_t st) {
   const int64_t lanes = total_words / WPL;
-  const dim3 grid((unsigned)((lanes + 255) / 256)), block(256);
+  const int64_t want = (lanes + 255) / 256;
+  const dim3 grid((unsigned)(want < kQuantBlocks ? want : kQuantBlocks)), block(256);
   if constexpr (WPL > 2) {
     if (T != 64) return hipErrorInvalidValue;
     quant_small_kernel<DT, 64, WPL><<<grid, block, 0, st>>>(W, packed, scales, zeros, lanes, intz);
