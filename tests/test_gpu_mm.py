@@ -76,6 +76,23 @@ def test_gemm_small(M, mode, g, transposed):
     assert_mm_close(host(y), O.matmul(a, *ref, K, transposed, bias), f"gemm M={M} {mode}{g} t={transposed}")
 
 
+# (g, K): the forward kernel's wide scale / zero loads cover 2, 4 or 8 contraction steps
+# depending on g and on K modulo 128 / 256 / 512
+WIDE_META_CASES = [(32, 1024), (32, 1152), (64, 1024), (64, 1280), (64, 1152), (128, 1536), (128, 1152)]
+
+
+@pytest.mark.parametrize("g,K", WIDE_META_CASES, ids=[f"g{g}-K{K}" for g, K in WIDE_META_CASES])
+def test_gemm_wide_meta_spans(g, K):
+    M, N = 160, 264
+    print(f"[case] gemm wide meta M={M} N={N} K={K} g={g}", flush=True)
+    _, ref, qw = _setup(709, g + K, N, K, "groupwise", g)
+    a = synth.activations_bf16(709, g + K, M, K)
+    bias = synth.bias_f32(709, g + K, N)
+    for split in (True, False):
+        y = w4.mm(dev_bf16(a), qw, bias=dev_f32(bias), split_k=split)
+        assert_mm_close(host(y), O.matmul(a, *ref, K, False, bias), f"wide meta g={g} K={K} split={split}")
+
+
 @pytest.mark.parametrize("M", [2, 8, 200])
 @pytest.mark.parametrize("transposed", [False, True], ids=["nt", "t"])
 def test_onehot_exact(M, transposed):
