@@ -19,7 +19,7 @@ Sources (web pages; cited by title and section):
 * "[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560):
   an fp32 bias added in the matmul epilogue.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 1. Scale and zero are min-max asymmetric: ``s = (max-min)/15``, ``z = -min/s``,
    computed in fp32 and stored as fp16 (round to nearest even); ``z`` is not
