@@ -84,6 +84,16 @@ def test_workspace_bytes():
         assert L.w4_workspace_bytes(ctypes.byref(d), op, 8192, ctypes.byref(b)) == 0 and b.value == 0
         assert "_splitk" not in w4.kernel_for(8192, 4096, 4096, "groupwise", 128, transposed=op == _lib.OP_MM_T)
     assert L.w4_workspace_bytes(ctypes.byref(d), 99, 4, ctypes.byref(b)) == _lib.W4_ERR_INVALID
+    # a partial last round: whole rounds of tile columns unsplit, the last columns split
+    # into compact planes [S][M][columns past the unsplit ones]
+    d = _lib.W4Desc(4096, 11008, _lib.MODE_ROWWISE, 0)
+    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM_T, 4096, ctypes.byref(b)) == 0
+    k = w4.kernel_for(4096, 4096, 11008, "rowwise", None, transposed=True)
+    assert "_tail" in k and "_splitk" in k
+    tail_cols = int(k.split("_tail", 1)[1].split("_", 1)[0])
+    S = int(k.rsplit("_splitk", 1)[1])
+    pw = 11008 - (11008 // 128 - tail_cols) * 128  # 128-column tiles, 11008 = 86 x 128
+    assert 0 < tail_cols < 86 and S >= 2 and b.value == S * 4096 * pw * 4
 
 
 def _mm(A, M, packed, s, z, desc, transposed=0, bias=None, Y=1024):
