@@ -322,12 +322,16 @@ GemvPlan plan(const MmArgs& a, const DeviceCaps& caps) {
   const int iters = (int)((a.K / 32 + 63) / 64);
   const size_t x_iter = (size_t)a.M * 4096;  // LDS bytes of X per 2048-column iteration
   // Tall weights: two rows per wave halve the X reads from LDS; one block per CU.
-  // Otherwise one row per wave, and two blocks per CU when the LDS allows it and each block
-  // still gets a row per wave (N >= 8192): below that, one block per CU measured faster
-  // (2048 x 2048: 8 % at every M; 4096 x 11008: up to 7 %), as X is staged half as often.
+  // Otherwise one row per wave, and two blocks per CU (twice the waves to hide latency)
+  // only for short rows (at most two 2048-column iterations) when each block still gets a
+  // row per wave (N >= 8192).  Otherwise one block per CU measured faster, X being staged
+  // half as often: 2048 x 2048 8 % at every M, 4096 x 11008 up to 7 %, 8192 x 8192 5-6 %
+  // at M = 2..4.
   p.R = a.N >= 16384 ? 2 : 1;
-  const int per_cu =
-      p.R == 1 && (size_t)iters * x_iter <= 72 * 1024 && a.N >= (int64_t)2 * caps.cus * kWaves ? 2 : 1;
+  const int per_cu = p.R == 1 && iters <= 2 && (size_t)iters * x_iter <= 72 * 1024 &&
+                             a.N >= (int64_t)2 * caps.cus * kWaves
+                         ? 2
+                         : 1;
   p.blocks = caps.cus * per_cu;
   p.rows_per_block = (int)((a.N + p.blocks - 1) / p.blocks);
   if (p.rows_per_block > 1024) p.rows_per_block = 1024;
