@@ -22,9 +22,15 @@ Also reported in the same JSON line (context, not `value`):
   cpu_baseline  the CPU oracle timed on a bounded sample of the GEMV sweep.
 
 Timing: the GPU is parked on a spin kernel while the host enqueues the whole
-batch, so the two HIP events around it measure back-to-back GPU execution, not
-host overhead.  The timed region is `steps` steps of the sweep; per-shape figures
-come from separate batches of 20 launches of one shape.
+batch, so the two HIP events around the timed part measure back-to-back GPU
+execution, not host overhead.  Every timed region is preceded, on the GPU
+timeline and with no gap, by an untimed lead-in of the same work (`warmup` steps
+of the sweep; >= 25 ms of the same launches elsewhere): for about the first 10 ms
+of work after an idle period the GPU's power management holds the rate 10-20%
+below its sustained value, and the lead-in takes the timed region past that
+transient.  The rate right after idle is reported beside `value` as context.
+The timed region is `steps` steps of the sweep; per-shape figures come from
+separate batches of 20 launches of one shape, each with its own lead-in.
 """
 
 from __future__ import annotations
@@ -70,21 +76,45 @@ def source_hash(*names: str) -> str:
     return h.hexdigest()[:16]
 
 
-def run_batch(torch, fns, spin_cycles: int | None = None) -> float:
-    """Run `fns` back-to-back behind a GPU spin (so the host enqueues ahead of the GPU);
-    returns the GPU time in ms from the first to the last launch (two events)."""
-    torch.cuda.synchronize()
-    if spin_cycles is None:
-        spin_cycles = int(2.4e9 * 100e-6 * len(fns)) + 2_000_000
-    torch.cuda._sleep(spin_cycles)
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for fn in fns:
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b)
+WARM_MS = 25.0  # untimed lead-in before every timed region, ms of GPU work
+
+
+def run_batch(torch, fns, warm=(), per_fn_s: float = 30e-6) -> float:
+    """Run `warm` then `fns` back-to-back behind a GPU spin (so the host enqueues ahead of
+    the GPU); returns the GPU time in ms of `fns` alone (two events after `warm`).
+
+    The spin is sized from a per-launch host budget; if the host took longer to enqueue than
+    the spin lasted, the GPU may have waited on it, so the batch is run again with a longer spin."""
+    n = len(warm) + len(fns)
+    for _ in range(4):
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        torch.cuda._sleep(int(2.4e9 * per_fn_s * n) + 2_000_000)
+        s1.record()
+        h0 = time.perf_counter()
+        for fn in warm:
+            fn()
+        a.record()
+        for fn in fns:
+            fn()
+        b.record()
+        host_ms = (time.perf_counter() - h0) * 1e3
+        torch.cuda.synchronize()
+        if host_ms < 0.9 * s0.elapsed_time(s1):
+            return a.elapsed_time(b)
+        per_fn_s *= 4
+    raise RuntimeError("the host could not enqueue the batch within the spin")
+
+
+def timed(torch, fns, warm_ms: float = WARM_MS) -> float:
+    """GPU ms of `fns`, run after an untimed lead-in of the same list repeated for >= warm_ms."""
+    est = run_batch(torch, fns)
+    reps = max(1, math.ceil(warm_ms / max(est, 1e-3)))
+    return run_batch(torch, fns, warm=list(fns) * reps)
 
 
 def clone_qw(w4, qw):
@@ -133,15 +163,27 @@ def bench_gemv(torch, w4, synth, args):
                 fns.append(fn)
         return fns
 
+    run_batch(torch, make_step())  # first launches: code objects loaded, kernel arguments set up
+    warm = []
     for _ in range(args.warmup):
-        run_batch(torch, make_step())
+        warm += make_step()
     fns = []
     for _ in range(args.steps):
         fns += make_step()
-    span = run_batch(torch, fns)  # the timed region: `steps` steps, launches back-to-back
+    # the timed region: `steps` steps, launches back-to-back, right behind `warmup` untimed steps
+    span = run_batch(torch, fns, warm=warm)
     n = len(launches)
     ms_per_step = span / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if args.sweep_only:
+        return {"value": value, "ms_per_step": ms_per_step, "step_bytes": step_bytes, "per_point_gbs": None,
+                "after_idle_gbs": None, "mean_launch_us": ms_per_step * 1e3 / n, "launches_per_step": n,
+                "points": [], "pool_copies": copies}
+    # context: the same number of steps timed right after an idle period, with no lead-in
+    idle_fns = []
+    for _ in range(args.steps):
+        idle_fns += make_step()
+    after_idle_gbs = step_bytes * args.steps / (run_batch(torch, idle_fns) * 1e-3) / 1e9
     # per-shape figures: 20 back-to-back launches of one point, rotating over enough
     # copies of that one weight that they cannot stay in the 256 MB last-level cache
     points = []
@@ -150,9 +192,13 @@ def bench_gemv(torch, w4, synth, args):
         b1 = N * K // 2 + 4 * N * (K // DECODE_G)
         extra = [clone_qw(w4, pool[0]) for _ in range(max(0, math.ceil(POINT_POOL_BYTES / b1) - len(pool)))]
         ppool = pool + extra
+        pctr = [0]
         for M in (1, 2, 3, 4):
-            batch = [lambda qw=ppool[i % len(ppool)], x=xs[M], y=ys[M]: w4.mm(x, qw, out=y) for i in range(20)]
-            t = run_batch(torch, batch) / len(batch)
+            def one(x=xs[M], y=ys[M], ppool=ppool):
+                qw = ppool[pctr[0] % len(ppool)]
+                pctr[0] += 1
+                w4.mm(x, qw, out=y)
+            t = timed(torch, [one] * 20) / 20
             point_ms.append(t)
             b = gemv_bytes(M, N, K, DECODE_G)
             points.append({"M": M, "N": N, "K": K, "us": round(t * 1e3, 3), "GBps": round(b / (t * 1e-3) / 1e9, 1),
@@ -162,6 +208,7 @@ def bench_gemv(torch, w4, synth, args):
     per_point_gbs = step_bytes / (sum(point_ms) * 1e-3) / 1e9
     return {
         "value": value, "ms_per_step": ms_per_step, "step_bytes": step_bytes, "per_point_gbs": per_point_gbs,
+        "after_idle_gbs": after_idle_gbs,
         "mean_launch_us": ms_per_step * 1e3 / n, "launches_per_step": n, "points": points,
         "pool_copies": copies,
     }
@@ -185,9 +232,8 @@ def bench_gemm(torch, w4, synth, reps: int):
                 dy = dev_bf16(torch, synth.activations_bf16(4, si * 10 + M, M, N, tensor_id=synth.T_DY))
                 y = torch.empty((M, N), dtype=torch.float32, device="cuda")
                 dx = torch.empty((M, K), dtype=torch.float32, device="cuda")
-                run_batch(torch, [lambda: w4.mm(x, qw, out=y), lambda: w4.mm(dy, qw, transposed=True, out=dx)])
-                t_nt = run_batch(torch, [lambda: w4.mm(x, qw, out=y)] * reps) / reps * 1e-3
-                t_t = run_batch(torch, [lambda: w4.mm(dy, qw, transposed=True, out=dx)] * reps) / reps * 1e-3
+                t_nt = timed(torch, [lambda: w4.mm(x, qw, out=y)] * reps) / reps * 1e-3
+                t_t = timed(torch, [lambda: w4.mm(dy, qw, transposed=True, out=dx)] * reps) / reps * 1e-3
                 fl = 2.0 * M * N * K
                 pts.append({"M": M, "N": N, "K": K, "mode": mode if g is None else f"g{g}",
                             "nt_tflops": round(fl / t_nt / 1e12, 1), "t_tflops": round(fl / t_t / 1e12, 1),
@@ -205,10 +251,9 @@ def bench_gemm(torch, w4, synth, reps: int):
                     ref = [lambda: w4.dequantize(qw, torch.bfloat16), lambda: F.linear(x, wd16),
                            lambda: torch.mm(dy, wd16)]
                     dense = [lambda: F.linear(x, wd16), lambda: torch.mm(dy, wd16)]
-                    run_batch(torch, ref + dense)
-                    t_f = run_batch(torch, fused * reps) / reps * 1e-3
-                    t_r = run_batch(torch, ref * reps) / reps * 1e-3
-                    t_d = run_batch(torch, dense * reps) / reps * 1e-3
+                    t_f = timed(torch, fused * reps) / reps * 1e-3
+                    t_r = timed(torch, ref * reps) / reps * 1e-3
+                    t_d = timed(torch, dense * reps) / reps * 1e-3
                     layer.append({"M": M, "N": N, "K": K, "fused_us": round(t_f * 1e6, 1),
                                   "dequant_ref_us": round(t_r * 1e6, 1), "dense_bf16_us": round(t_d * 1e6, 1)})
                     del wd16
@@ -249,7 +294,7 @@ def bench_quantize(torch, w4, synth, reps: int):
     out = []
     for mode, g in QUANT_MODES:
         qw = w4.quantize_pack(wd, mode, g)
-        t = run_batch(torch, [lambda: w4.quantize_pack(wd, mode, g)] * reps) / reps * 1e-3
+        t = timed(torch, [lambda: w4.quantize_pack(wd, mode, g)] * reps) / reps * 1e-3
         pairs = 1 if mode == "global" else (N if mode == "rowwise" else N * K // g)
         reads = 2 if mode == "global" else 1
         nbytes = reads * N * K * 2 + N * K // 2 + 4 * pairs
@@ -318,12 +363,15 @@ def load_traffic(step_bytes_per_launch: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=60, help="untimed steps run right before the timed ones")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="skip the GEMM and quantize blocks")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--details", default=None, help="write per-point results (JSON) to this path")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="time the sweep alone (no per-shape batches or after-idle figure): every point is then "
+                         "launched equally often, as counter passes need")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -353,7 +401,9 @@ def main() -> int:
         log("copy calibration: 268435456 bytes read and written once")
 
     g = bench_gemv(torch, w4, synth, args)
-    log(f"GEMV sweep: {g['value']:.1f} GB/s per step; per-shape batches {g['per_point_gbs']:.1f} GB/s")
+    log(f"GEMV sweep: {g['value']:.1f} GB/s per step" + ("" if args.sweep_only else
+        f"; per-shape batches {g['per_point_gbs']:.1f} GB/s; first {args.steps} steps after idle "
+        f"{g['after_idle_gbs']:.1f} GB/s"))
     per_launch_bytes = g["step_bytes"] / g["launches_per_step"]
     traffic = load_traffic(per_launch_bytes)
     result = {
@@ -381,11 +431,12 @@ def main() -> int:
                      "frac": round(per_launch_bytes / (g["mean_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "mean_launch_us": round(g["mean_launch_us"], 3),
                      "algorithmic_bytes_per_launch": round(per_launch_bytes, 1),
-                     "per_shape_batches_gbs": round(g["per_point_gbs"], 1)},
+                     "per_shape_batches_gbs": None if args.sweep_only else round(g["per_point_gbs"], 1),
+                     "sweep_after_idle_gbs": None if args.sweep_only else round(g["after_idle_gbs"], 1)},
     }
     details = {"gemv": g["points"]}
     if not args.no_extras:
-        gm = bench_gemm(torch, w4, synth, reps=5)
+        gm = bench_gemm(torch, w4, synth, reps=10)
         result["gemm"] = {k: v for k, v in gm.items() if k not in ("points", "layer_points")}
         result["gemm"]["roofline"] = {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                       "achieved_nt": gm["nt_tflops"], "achieved_t": gm["t_tflops"],
@@ -393,7 +444,7 @@ def main() -> int:
         details["gemm"] = gm["points"]
         details["qlora_layer"] = gm["layer_points"]
         log(f"GEMM: NT {gm['nt_tflops']} TFLOP/s, T {gm['t_tflops']} TFLOP/s, T/NT {gm['t_over_nt_total']}")
-        qz = bench_quantize(torch, w4, synth, reps=5)
+        qz = bench_quantize(torch, w4, synth, reps=10)
         result["quantize"] = {"workload": qz["workload"],
                               "GBps": {p["mode"]: p["GBps"] for p in qz["points"]},
                               "mae": {p["mode"]: p["mae"] for p in qz["points"]},
