@@ -6,7 +6,9 @@
 // on gfx950 with no matrix cores):
 //   * one workgroup (16 waves) per contiguous block of rows, about one block per CU:
 //     X is staged into LDS once per workgroup (in phases of up to PW x 2048 columns
-//     when M*K does not fit), so activation traffic does not grow with N;
+//     when M*K does not fit), so activation traffic does not grow with N; the staging
+//     uses direct global -> LDS loads issued ahead of the first weight loads, so the
+//     first product waits for X and not for the weights behind it;
 //   * each wave streams row groups of R rows over K; lane l owns the 16-byte chunk
 //     c = it*64 + l of a row (32 codes), so one wave-wide load is 1 KB contiguous;
 //   * weights, scales and zeros come in through buffer loads whose per-lane offset
@@ -203,6 +205,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int kLoadsPerStep = R * (1 + 2 * GPC);  // vector-memory instructions of one load()
+  static_assert(kLoadsPerStep < 64, "vmcnt holds 6 bits");
   Stage<R, GPC> A, B;
   for (int p0 = 0; p0 < iters; p0 += PW) {
     const int pw = min(PW, iters - p0);
@@ -215,19 +220,34 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
         ++k;
       }
     };
+    // X columns of this phase -> LDS by direct loads (no staging registers, no LDS store
+    // instructions), issued ahead of the phase's first weight loads so that the barrier
+    // below waits for X alone.  Row j of the tile (iteration il, row m, word w) is one
+    // wave-wide load: lane c fills slot 64 j + c.  Chunks past K are zeroed by stores.
+    if (p0 > 0) __syncthreads();  // every wave is done with the previous phase's X
+    const int nj = pw * M * 4;
+    for (int j = wave; j < nj; j += kWaves) {
+      const int il = j / (M * 4), rj = j - il * (M * 4), m = rj >> 2, w = rj & 3;
+      const int col = ((p0 + il) * 64 + lane) * 32 + w * 8;
+      if (col < K)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(X + (size_t)m * K, (uint32_t)K * 2),
+                                                 (lds_void*)(xs + j * 64), 16, col * 2, 0, 0, 0);
+      else
+        xs[j * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
     load(lk, p0 + lit, A);
     advance(lk, lit);
-
-    // X columns of this phase -> LDS, zero beyond K
-    if (p0 > 0) __syncthreads();  // every wave is done with the previous phase's X
-    const int units = pw * M * 256;
-    for (int u = tid; u < units; u += T) {
-      const int c = u & 63, w = (u >> 6) & 3, mi = u >> 8;
-      const int il = mi / M, m = mi - il * M;
-      const int col = ((p0 + il) * 64 + c) * 32 + w * 8;
-      xs[u] = col < K ? *reinterpret_cast<const u32x4*>(X + (size_t)m * K + col) : u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
+    // Loads complete in issue order: X has landed once at most the one step of weight loads
+    // issued after it is outstanding; the zero stores by lgkmcnt(0).  The barrier carries no
+    // fence, which would also wait for those weight loads; the clobbers keep memory
+    // accesses, and the scheduling barriers keep all instructions, on their side of it.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((kLoadsPerStep & 15) | 0x70 | ((kLoadsPerStep >> 4) << 14));  // vmcnt(n) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     auto compute = [&](const Stage<R, GPC>& st) {
       DqConst dc[R][GPC];
