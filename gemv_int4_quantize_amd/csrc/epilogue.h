@@ -44,4 +44,66 @@ __device__ __forceinline__ void epi_put(const Epi& e, const EpiCol& col, int64_t
   else *reinterpret_cast<uint16_t*>(q) = f32_to_f16_bits(v);
 }
 
+// fp32 output in one segment with 16-byte aligned rows: four consecutive columns go out
+// as one 16-byte store (outc = output columns).
+__device__ __forceinline__ bool epi_wide_f32(const Epi& e, int64_t outc) {
+  return e.dt == W4_DT_F32 && e.nseg == 1 && (outc & 3) == 0 && (e.ld[0] & 3) == 0 &&
+         (reinterpret_cast<uintptr_t>(e.y[0]) & 15) == 0;
+}
+
+// Columns c4 .. c4 + 3 of such an output: row 0, row stride and the four biases.
+struct EpiQuad {
+  float* y;
+  int64_t ld;
+  float b[4];
+  bool ok;  // the four columns lie inside the output
+};
+
+__device__ __forceinline__ EpiQuad epi_quad(const Epi& e, int64_t c4, int64_t outc) {
+  EpiQuad q;
+  q.ok = c4 < outc;
+  q.y = static_cast<float*>(e.y[0]) + c4;
+  q.ld = e.ld[0];
+  const float* bias = static_cast<const float*>(e.bias);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) q.b[u] = bias != nullptr && q.ok ? bias[c4 + u] : 0.0f;
+  return q;
+}
+
+// One 32x32 result block of v_mfma_f32_32x32x16 (register r of lane l: row row0 +
+// 8 (r / 4) + 4 (l / 32) + (r % 4), column l % 32 of the block) + bias, stored 16 bytes at a
+// time.  A 4x4 transpose within each lane quad (two DPP quad-permute exchanges) leaves
+// lane (k, s) of a half-wave with row s of every 4-row group for the quad's columns
+// 4k .. 4k + 3, the columns of q.  The values are those epi_put stores, bit for bit; the
+// stores are non-temporal (the output is not read again by this kernel).  Every lane of
+// the wave must call it (DPP); rows past M are skipped.  row0 includes the 4 (l / 32) term.
+__device__ __forceinline__ void epi_put_block_wide(const EpiQuad& q, const f32x16& acc, int64_t row0, int64_t M,
+                                                   int lane) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const int s = lane & 3;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float v[4], p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = acc[g * 4 + t];
+    // rows of the lane pair (s, s ^ 2): keep the diagonal 2x2 blocks, swap the others
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      p[t] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[t ^ 2]), 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = ((s & 2) == 0) == (t < 2) ? v[t] : p[t];
+    // within the 2x2 blocks, lane pair (s, s ^ 1)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      p[t] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[t ^ 1]), 0xB1, 0xF, 0xF, false));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = (s & 1) == (t & 1) ? v[t] : p[t];
+    const int64_t m = row0 + g * 8 + s;
+    if (q.ok && m < M) {
+      const f32x4v o = {v[0] + q.b[0], v[1] + q.b[1], v[2] + q.b[2], v[3] + q.b[3]};
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4v*>(q.y + m * q.ld));
+    }
+  }
+}
+
 }  // namespace w4

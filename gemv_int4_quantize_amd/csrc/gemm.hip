@@ -568,6 +568,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   // through the output epilogue (bias, output dtype, output segments).
   const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
   const int cbase = c0 + wn * FN * 32 + lr;
+  if (part == nullptr && epi_wide_f32(ep, OUTC)) {  // plain fp32 output: 16-byte stores
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const EpiQuad q = epi_quad(ep, cbase - lr + j * 32 + (lr & ~3), OUTC);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) epi_put_block_wide(q, acc[i][j], rbase + i * 32, M, lane);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = cbase + j * 32;

@@ -400,8 +400,18 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
 
   // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
   // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][pw] plane,
-  // an unsplit launch stores through the output epilogue
+  // an unsplit launch stores through the output epilogue (16 bytes at a time for a plain
+  // fp32 output)
   const int rbase = m0 + h * 4;
+  if (part == nullptr && epi_wide_f32(ep, N)) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const EpiQuad q = epi_quad(ep, n0w + j * 32 + (lr & ~3), N);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) epi_put_block_wide(q, acc[i][j], rbase + i * 32, M, lane);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int c = n0w + j * 32 + lr;

@@ -128,3 +128,35 @@ def test_segments_into_strided_views(M, tr):
         mask[:, c + (i + 1) * pad: c + (i + 1) * pad + n] = False
         c += n
     assert np.all(hb[mask] == -7.25)
+
+
+@pytest.mark.parametrize("M,tr", [(300, False), (1024, False), (300, True), (1024, True)])
+def test_fp32_output_layouts(M, tr):
+    """An unsplit fp32 output is stored four columns at a time when its rows are 16-byte
+    aligned (a lane-quad transpose of the MFMA result), else one value at a time.  Every
+    layout gives the same bits as the contiguous output, with and without a bias, and
+    leaves the memory around a view untouched."""
+    N, K = 1024, 2048
+    w = synth.weight(723, M, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), O.ROWWISE)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), "rowwise")
+    outc = K if tr else N
+    a_bits = synth.activations_bf16(723, M, M, N if tr else K)
+    a = dev_bf16(a_bits)
+    b32 = synth.bias_f32(723, M, outc)
+    ref64 = O.matmul(a_bits, *ref, K, tr)
+    for bias in (None, _dev_vec(b32, "f32")):
+        want = w4.mm(a, qw, transposed=tr, bias=bias, split_k=False)
+        bref = np.zeros(outc) if bias is None else b32.astype(np.float64)
+        assert_mm_close(host(want), ref64 + bref, f"contiguous M={M} t={tr}")
+        # (first column offset in floats, row stride): aligned rows with padding, a base one
+        # float past alignment, and a row stride that is not a multiple of four
+        for off, ld in ((4, outc + 8), (1, outc + 8), (0, outc + 1)):
+            buf = torch.full((M, ld), -7.25, dtype=torch.float32, device=DEV)
+            view = buf[:, off:off + outc]
+            w4.mm_split(a, qw, [view], bias=bias, transposed=tr, split_k=False)
+            assert torch.equal(view, want), (off, ld, bias is None)
+            hb = host(buf)
+            mask = np.ones(hb.shape, dtype=bool)
+            mask[:, off:off + outc] = False
+            assert np.all(hb[mask] == -7.25), (off, ld)
