@@ -13,6 +13,10 @@ Weights rotate through >= 1 GiB of distinct copies so no launch finds its
 weights in the 256 MB Infinity Cache.
 
 Also reported in the same JSON line (context, not `value`):
+  prefill   forward GEMM at Llama-3.2-1B-like shapes: M in {128, 512, 2048},
+            (N,K) in {(2048,2048), (8192,2048), (2048,8192), (512,2048), (128256,2048)},
+            global / rowwise / g=64, fp32 bias; TFLOP/s overall, by M, and the minimum
+            at M >= 512.
   gemm      QLoRA pair at Llama-2-7B layer shapes: M in {1024, 2048, 4096},
             (N,K) in {(12288,4096) fused QKV, (11008,4096), (4096,11008)}, rowwise
             and g=64, forward Y = X w^T and transposed dX = dY w on one packed buffer;
@@ -25,7 +29,7 @@ Timing: the GPU is parked on a spin kernel while the host enqueues the whole
 batch, so the two HIP events around the timed part measure back-to-back GPU
 execution, not host overhead.  Every timed region is preceded, on the GPU
 timeline and with no gap, by an untimed lead-in of the same work (`warmup` steps
-of the sweep; >= 25 ms of the same launches elsewhere): for about the first 10 ms
+of the sweep; >= 25 ms of the same launches elsewhere, at most 1000 calls): for about the first 10 ms
 of work after an idle period the GPU's power management holds the rate 10-20%
 below its sustained value, and the lead-in takes the timed region past that
 transient.  The rate right after idle is reported beside `value` as context.
@@ -110,10 +114,17 @@ def run_batch(torch, fns, warm=(), per_fn_s: float = 30e-6) -> float:
     raise RuntimeError("the host could not enqueue the batch within the spin")
 
 
+# While the spin runs, the launch queue takes about 2000 packets before the host blocks
+# (measured: 1000 calls of a split-K GEMM, two kernels each, enqueue at ~15 us per call;
+# 2000 such calls block until the spin ends).
+MAX_LEAD_CALLS = 1000
+
+
 def timed(torch, fns, warm_ms: float = WARM_MS) -> float:
-    """GPU ms of `fns`, run after an untimed lead-in of the same list repeated for >= warm_ms."""
+    """GPU ms of `fns`, run after an untimed lead-in of the same list repeated for >= warm_ms
+    (or for MAX_LEAD_CALLS calls, whichever is shorter)."""
     est = run_batch(torch, fns)
-    reps = max(1, math.ceil(warm_ms / max(est, 1e-3)))
+    reps = max(1, min(math.ceil(warm_ms / max(est, 1e-3)), MAX_LEAD_CALLS // len(fns)))
     return run_batch(torch, fns, warm=list(fns) * reps)
 
 
@@ -285,6 +296,47 @@ def bench_gemm(torch, w4, synth, reps: int):
     }
 
 
+PREFILL_SHAPES = [(2048, 2048), (8192, 2048), (2048, 8192), (512, 2048), (128256, 2048)]
+PREFILL_M = [128, 512, 2048]
+
+
+def bench_prefill(torch, w4, synth, reps: int):
+    """Prefill GEMM at Llama-3.2-1B-like shapes, three scale modes, fp32 bias epilogue."""
+    log("prefill GEMM: 5 shapes x {global, rowwise, g64} x M in {128, 512, 2048}, fp32 bias")
+    pts = []
+    for si, (N, K) in enumerate(PREFILL_SHAPES):
+        wd = dev_bf16(torch, synth.weight(3, si, N, K, "bf16"))
+        bias = torch.from_numpy(synth.bias_f32(3, si, N)).cuda()
+        for mode, g in [("global", None), ("rowwise", None), ("groupwise", 64)]:
+            qw = w4.quantize_pack(wd, mode, g)
+            for M in PREFILL_M:
+                x = dev_bf16(torch, synth.activations_bf16(3, si * 10 + M, M, K))
+                y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                t = timed(torch, [lambda: w4.mm(x, qw, bias=bias, out=y)] * reps) / reps * 1e-3
+                fl = 2.0 * M * N * K
+                pts.append({"M": M, "N": N, "K": K, "mode": mode if g is None else f"g{g}", "us": round(t * 1e6, 1),
+                            "tflops": round(fl / t / 1e12, 1), "kernel": w4.kernel_for(M, N, K, mode, g)})
+                del x, y
+            del qw
+        del wd, bias
+        torch.cuda.empty_cache()
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
+    t = sum(p["us"] for p in pts) * 1e-6
+    by_m = {}
+    for M in PREFILL_M:
+        sel = [p for p in pts if p["M"] == M]
+        by_m[str(M)] = round(sum(2.0 * p["M"] * p["N"] * p["K"] for p in sel) / (sum(p["us"] for p in sel) * 1e-6)
+                             / 1e12, 1)
+    big = [p for p in pts if p["M"] >= 512]
+    return {
+        "workload": "prefill GEMM, Llama-3.2-1B-like shapes, global / rowwise / g64, fp32 bias",
+        "tflops": round(fl / t / 1e12, 1), "frac_of_peak": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "tflops_by_M": by_m,
+        "min_tflops_m_ge_512": min(p["tflops"] for p in big),
+        "points": pts,
+    }
+
+
 def bench_quantize(torch, w4, synth, reps: int):
     import numpy as np
     N, K = 128256, 2048
@@ -444,6 +496,11 @@ def main() -> int:
         details["gemm"] = gm["points"]
         details["qlora_layer"] = gm["layer_points"]
         log(f"GEMM: NT {gm['nt_tflops']} TFLOP/s, T {gm['t_tflops']} TFLOP/s, T/NT {gm['t_over_nt_total']}")
+        pf = bench_prefill(torch, w4, synth, reps=10)
+        result["prefill"] = {k: v for k, v in pf.items() if k != "points"}
+        details["prefill"] = pf["points"]
+        log(f"prefill GEMM: {pf['tflops']} TFLOP/s over the 45 points, by M {pf['tflops_by_M']}, "
+            f"M >= 512 minimum {pf['min_tflops_m_ge_512']}")
         qz = bench_quantize(torch, w4, synth, reps=10)
         result["quantize"] = {"workload": qz["workload"],
                               "GBps": {p["mode"]: p["GBps"] for p in qz["points"]},
