@@ -665,6 +665,49 @@ struct Plan {
 // utilisation x edge-tile useful fraction / (1 + cost of the split-K partial planes).
 // Utilisation: with all workgroups resident at once, min(1, workgroups / (CUs x full));
 // over several rounds, the filled fraction of the rounds.
+// Small forward problems at prefill sizes (M >= 128, under kSmallFlops: a few tens of
+// microseconds; the short-M tiles keep their measured scores) are bound by the
+// latency of each contraction step and by launch costs, not by the MFMA rate that the scores
+// of pick_plan model, so an estimated time picks their plan.  A round of workgroups takes the
+// longer of its contraction steps at the latency of one step and its share of the CU's MFMA
+// rate at the tile's efficiency; a split adds the reduction launch and the write and read of
+// its fp32 partial planes.  Constants measured on MI355X: a latency-bound step ~0.4 us (32 x
+// 128 and 64 x 128 tiles, one round, K = 2048), the best tile ~1.05 PFLOP/s at eff = 1, the
+// reduction launch ~3 us, partial planes at ~4 TB/s.  At M = 512, (N, K) = (2048, 2048) an
+// unsplit 32 x 128 launch took 12.9 us against 19.0 us for the two-way split the scores chose.
+constexpr double kSmallFlops = 2e10;
+constexpr double kStepS = 0.4e-6, kPeakFlops = 1.05e15, kReduceLaunchS = 3e-6, kPlaneBps = 4e12;
+
+Plan pick_plan_small(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
+  const bool reg_ok = gemm_nt_reg_supported(a);
+  const int64_t cus = caps.cus > 0 ? caps.cus : 256;
+  Plan best{reg_ok ? 3 : kNtLdsCfg, 1};
+  double best_t = 1e30;
+  for (int i = 0; i < kNumCfgs; ++i) {
+    const Cfg& c = kCfgs[i];
+    if (c.transposed || (c.kind != 0) != reg_ok) continue;
+    const int64_t bm = c.wm * c.fm * 32, bn = c.wn * c.fn * 32;
+    const int64_t tm = (a.M + bm - 1) / bm, tn = (a.N + bn - 1) / bn;
+    const int64_t kt = (a.K + c.bk - 1) / c.bk;
+    for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
+      if (sp > 1 && kt / sp < 16) break;  // keep >= 16 contraction steps per slice
+      const int64_t wgs = tm * tn * sp, steps = (kt + sp - 1) / sp;
+      const int64_t rounds = (wgs + cus * c.slots - 1) / (cus * c.slots);
+      const int64_t per_cu = std::min<int64_t>(c.slots, (wgs + cus - 1) / cus);
+      const double wg_flops = 2.0 * bm * bn * steps * c.bk;
+      const double t_round = std::max(steps * kStepS, per_cu * wg_flops / (c.eff * kPeakFlops / cus));
+      const double t = rounds * t_round + (sp > 1 ? kReduceLaunchS + 8.0 * sp * a.M * a.N / kPlaneBps : 0.0);
+      // ties (both latency-bound) go to the later, smaller tile: measured 3-4% faster at
+      // M = 128, (2048, 2048) and M = 512, (512, 2048)
+      if (t <= best_t) {
+        best_t = t;
+        best = Plan{i, sp};
+      }
+    }
+  }
+  return best;
+}
+
 Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
   static const int forced = [] {
     // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
@@ -673,6 +716,8 @@ Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
   }();
   const int64_t outc = a.transposed ? a.K : a.N;
   const int64_t L = a.transposed ? a.N : a.K;
+  if (forced < 0 && !a.transposed && a.M >= 128 && 2.0 * a.M * outc * L < kSmallFlops)
+    return pick_plan_small(a, caps, allow_split);
   const bool reg_ok = gemm_nt_reg_supported(a);
   const int64_t cus = caps.cus > 0 ? caps.cus : 256;
   Plan best{a.transposed ? 1 : (reg_ok ? 3 : kNtLdsCfg), 1};
