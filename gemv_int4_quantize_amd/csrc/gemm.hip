@@ -636,7 +636,7 @@ struct Cfg {
   float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 0.9f},
+    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 1.06f},
     {0, 4, 2, 2, 2, 64, 4, "gemm_t_256x128", true, 1, 1, 1.0f},
     {0, 2, 2, 2, 2, 32, 4, "gemm_t_128x128", true, 3, 2, 0.65f},
     {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 0.92f},
