@@ -87,13 +87,15 @@ def test_workspace_bytes():
     # a partial last round: whole rounds of tile columns unsplit, the last columns split
     # into compact planes [S][M][columns past the unsplit ones]
     d = _lib.W4Desc(4096, 11008, _lib.MODE_ROWWISE, 0)
-    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM_T, 4096, ctypes.byref(b)) == 0
-    k = w4.kernel_for(4096, 4096, 11008, "rowwise", None, transposed=True)
-    assert "_tail" in k and "_splitk" in k
-    tail_cols = int(k.split("_tail", 1)[1].split("_", 1)[0])
-    S = int(k.rsplit("_splitk", 1)[1])
-    pw = 11008 - (11008 // 128 - tail_cols) * 128  # 128-column tiles, 11008 = 86 x 128
-    assert 0 < tail_cols < 86 and S >= 2 and b.value == S * 4096 * pw * 4
+    for M in (3072, 8192):  # dX [M][11008]: 128- or 256-column tiles, 11008 = 86 x 128 = 43 x 256
+        assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM_T, M, ctypes.byref(b)) == 0
+        k = w4.kernel_for(M, 4096, 11008, "rowwise", None, transposed=True)
+        assert "_tail" in k and "_splitk" in k, k
+        bn = int(k.split("_tail", 1)[0].rsplit("x", 1)[1])
+        tail_cols = int(k.split("_tail", 1)[1].split("_", 1)[0])
+        S = int(k.rsplit("_splitk", 1)[1])
+        pw = 11008 - (11008 // bn - tail_cols) * bn
+        assert 0 < tail_cols < 11008 // bn and S >= 2 and b.value == S * M * pw * 4
 
 
 def _mm(A, M, packed, s, z, desc, transposed=0, bias=None, Y=1024):
