@@ -424,6 +424,8 @@ def main() -> int:
     ap.add_argument("--sweep-only", action="store_true",
                     help="time the sweep alone (no per-shape batches or after-idle figure): every point is then "
                          "launched equally often, as counter passes need")
+    ap.add_argument("--gemm-only", action="store_true",
+                    help="run only the QLoRA GEMM block and print its figures (for counter passes over the GEMM kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device-to-device copy (a known-size reference for HBM counters)")
     args = ap.parse_args()
@@ -452,6 +454,10 @@ def main() -> int:
         del src, dst
         log("copy calibration: 268435456 bytes read and written once")
 
+    if args.gemm_only:
+        gm = bench_gemm(torch, w4, synth, reps=10)
+        print(json.dumps({k: v for k, v in gm.items() if k not in ("points", "layer_points")}), flush=True)
+        return 0
     g = bench_gemv(torch, w4, synth, args)
     log(f"GEMV sweep: {g['value']:.1f} GB/s per step" + ("" if args.sweep_only else
         f"; per-shape batches {g['per_point_gbs']:.1f} GB/s; first {args.steps} steps after idle "
