@@ -299,14 +299,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
     };
 
     // two slots, unrolled by two: the slot being filled is never the one being read,
-    // and every iteration issues exactly one step of loads (exact wait counts)
+    // and every iteration issues exactly one step of loads (exact wait counts).  A wave
+    // raises its priority while it issues a step's loads, so the sequencer lets loads out
+    // ahead of other waves' dequantization (measured: decode sweep +1.5%)
     int t = 0;
     for (; t + 2 <= steps; t += 2) {
+      __builtin_amdgcn_s_setprio(2);
       load(lk, p0 + lit, B);
       advance(lk, lit);
+      __builtin_amdgcn_s_setprio(0);
       compute(A);
+      __builtin_amdgcn_s_setprio(2);
       load(lk, p0 + lit, A);
       advance(lk, lit);
+      __builtin_amdgcn_s_setprio(0);
       compute(B);
     }
     if (t < steps) compute(A);
