@@ -61,8 +61,16 @@ __device__ __forceinline__ QParams qparams(float lo, float hi, bool intz) {
   // backend turns `0.0f - lo` into a negate modifier, which yields -0 for lo == +0.
   const float nlo = lo == 0.0f ? 0.0f : -lo;
   const float z32 = nlo / s;
-  const uint16_t zb = intz ? f32_to_f16_bits(__builtin_fminf(__builtin_fmaxf(__builtin_rintf(z32), 0.0f), 15.0f))
-                           : f32_to_f16_bits(z32);
+  uint16_t zb = intz ? f32_to_f16_bits(__builtin_fminf(__builtin_fmaxf(__builtin_rintf(z32), 0.0f), 15.0f))
+                     : f32_to_f16_bits(z32);
+  if (!intz && (zb & 0x7FFFu) == 0x7C00u) {
+    // The zero point overflowed fp16: the group's range is below 15 |min| / 65504, tiny next
+    // to its offset (reachable with fp32 weights only).  It is quantized as a constant
+    // group: s = 1, z = fp16(0 - min).
+    sb = 0x3C00;
+    s = 1.0f;
+    zb = f32_to_f16_bits(nlo);
+  }
   QParams p;
   p.s = s;
   p.z = f16_bits_to_f32(zb);

@@ -24,6 +24,11 @@ Readings where the pages are silent:
 1. Scale and zero are min-max asymmetric: ``s = (max-min)/15``, ``z = -min/s``,
    computed in fp32 and stored as fp16 (round to nearest even); ``z`` is not
    rounded to an integer.  A zero or non-finite fp16 scale is replaced by 1.
+7. A group whose fp16 zero would be infinite (its range below 15 |min| / 65504,
+   e.g. [1.0, 1.0001] in fp32) is quantized like a constant group: s = 1 and
+   ``z = fp16(0 - min)``, so its values dequantize to within its range of min.
+   Only when |min| > 65504 (possible for fp32 / bf16 weights) does that zero
+   overflow too; it is then left infinite.
 2. Codes: ``q = clamp(rint(w/s + z), 0, 15)`` with fp32 divide and add and
    round-half-to-even.
 3. Packing: row-major ``[N][K/8]`` int32 words; code ``k = 8c + j`` of row n
@@ -48,14 +53,20 @@ Pins (tests/test_oracle_*.py, run with ``-m "not gpu"``):
   in [0, 15], exact zero maps to code z and dequantizes to exactly 0).
 * dequantize: all 16 codes against an exact-rational bf16 rounding (and fp16
   rounding for the fp16 operand).
-* matmul: exact-rational triple loop on tiny shapes, one-hot pins of the layout
-  in both modes, constant-code closed form, linearity and bias.
+* matmul: exact-rational triple loop on tiny shapes (bf16 activations, and fp16
+  activations decoded by hand from their bit fields against the fp16 operand),
+  one-hot pins of the layout in both modes, constant-code closed form,
+  linearity and bias.
 * fused QKV: column concatenation (non-transposed) and sum (transposed).
 * round_output: hand-derived bf16 / fp16 roundings (ties to even, 8 and 11
   significant bits, the fp16 maximum).
 * compression: the page's printed column reproduced by its closed form.
-* MAE: parity unpinned (the page's data distribution is unstated); only its
-  trends are checked.
+* MAE: a hand-derived value on two golden rows (tests/golden/mae_rows.txt) that
+  tells the fp32 dequantization from the bf16 one and an absolute mean from a
+  signed or squared one; the page's own MAE values stay unpinned (its data
+  distribution is unstated), only their trends are checked.
+* zero overflow (reading 7): a group built so that -min/s overflows fp16, and
+  the exact-rational brute force over such groups.
 """
 
 from __future__ import annotations
@@ -145,6 +156,14 @@ def quantize(w32: np.ndarray, mode: int, g: int | None = None, int_zero: bool = 
             t = np.rint(grp / s_f[..., None]) + z_f[..., None]  # round, then the exact integer add
         else:
             z16 = z32.astype(_F16)
+            # A zero point beyond the fp16 range (the group's range is below 15 |min| / 65504,
+            # tiny next to its offset) makes the group degenerate like a zero scale: s = 1
+            # and z = fp16(0 - min), so its values dequantize to min (reading 7).
+            wide = ~np.isfinite(z16)
+            if np.any(wide):
+                s16 = np.where(wide, _F16(1.0), s16)
+                s_f = s16.astype(_F32)
+                z16 = np.where(wide, ((_F32(0.0) - lo) / s_f).astype(_F16), z16)
             z_f = z16.astype(_F32)
             t = grp / s_f[..., None] + z_f[..., None]  # two fp32 ops, each rounded
     assert not np.any(np.isnan(t)), "code argument is NaN (zero overflowed fp16)"

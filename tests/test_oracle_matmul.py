@@ -45,6 +45,43 @@ def test_bruteforce_tiny(transposed, mode, g, with_bias):
     assert np.allclose(y, ye, rtol=1e-13, atol=1e-13)
 
 
+def _f16_bits_fraction(b: int) -> Fraction:
+    """Exact value of an fp16 bit pattern, decoded from the format's fields (1 sign bit,
+    5 exponent bits with bias 15, 10 fraction bits; exponent 0 is subnormal)."""
+    sign = -1 if b >> 15 else 1
+    e, f = (b >> 10) & 31, b & 1023
+    assert e != 31, "finite values only"
+    if e == 0:
+        return sign * Fraction(f, 1024) * Fraction(1, 2**14)
+    return sign * (1 + Fraction(f, 1024)) * Fraction(2) ** (e - 15)
+
+
+@pytest.mark.parametrize("transposed", [False, True])
+@pytest.mark.parametrize("mode,g", [(O.ROWWISE, None), (O.GROUPWISE, 16)])
+def test_bruteforce_tiny_f16(transposed, mode, g):
+    """fp16 activations: every product of the fp16 operand fp16_rne(fp32(q - z) * s) with
+    hand-decoded fp16 activations, summed exactly, against matmul(a_dtype="f16")."""
+    from exact import round_fmt
+    N, K, M = 8, 32, 3
+    packed, s, z = _case(N, K, mode, g, 7)
+    q = O.unpack(packed)
+    gs = K if mode == O.ROWWISE else g
+    wq = [[round_fmt(round_fmt(round_fmt(Fraction(int(q[n, k])) - Fraction(float(z[n, k // gs])), "f32")
+                               * Fraction(float(s[n, k // gs])), "f32"), "f16") for k in range(K)]
+          for n in range(N)]
+    L = N if transposed else K
+    a = (np.random.default_rng(8).standard_normal((M, L)) * 2).astype(np.float16).view(np.uint16)
+    a[0, 0] = 0x0001  # the smallest fp16 subnormal
+    a[1, 1] = 0x8400  # -2^-14, the smallest normal, negative
+    af = [[_f16_bits_fraction(int(v)) for v in row] for row in a]
+    if transposed:
+        ye = [[sum(af[m][n] * wq[n][k] for n in range(N)) for k in range(K)] for m in range(M)]
+    else:
+        ye = [[sum(af[m][k] * wq[n][k] for k in range(K)) for n in range(N)] for m in range(M)]
+    y = O.matmul(a, packed, s, z, K, transposed, a_dtype="f16")
+    assert np.allclose(y, np.array([[float(v) for v in row] for row in ye]), rtol=1e-13, atol=1e-13)
+
+
 def _bf16_onehot(M, L, idx):
     x = np.zeros((M, L), dtype=np.uint16)
     x[0, idx] = 0x3F80  # 1.0

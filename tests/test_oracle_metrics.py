@@ -1,5 +1,6 @@
 """Pins of the oracle's reported quantities: compression (closed form, and the
-page's printed column) and MAE (trend only: parity unpinned)."""
+page's printed column) and MAE (a hand-derived value on two golden rows, and the
+page's trend; the page's own MAE values stay unpinned, their data being unstated)."""
 
 import os
 
@@ -52,3 +53,35 @@ def test_mae_trend_matches_page():
     assert all(a < b for a, b in zip(seq, seq[1:]))
     assert glob > max(seq)
     assert row == pytest.approx(maes[4096], rel=1e-12)
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.split()
+    return out
+
+
+def test_mae_hand_derived_rows():
+    """MAE of two ROWWISE rows derived by hand (tests/golden/mae_rows.txt).  A signed mean, a
+    squared error, a sum instead of a mean, or the bf16 operand in place of the fp32
+    dequantization each gives a different value."""
+    gd = _golden("mae_rows.txt")
+    a = np.array([float(v) for v in gd["row_a"]], dtype=np.float32)
+    b = np.array([float(v) for v in gd["row_b"]], dtype=np.float32)
+    # the decimal inputs of row A are within 3e-7 of their fp32 values: 1e-7 on a mean of 16
+    for row, key in ((a, "mae_a"), (b, "mae_b")):
+        w = row.reshape(1, 16)
+        assert O.mae(w, *O.quantize_pack(w, O.ROWWISE)) == pytest.approx(float(gd[key][0]), abs=1e-7)
+    w = np.stack([a, b])
+    packed, s, z = O.quantize_pack(w, O.ROWWISE)
+    assert int(s.view(np.uint16)[1, 0]) == int(gd["scale_bits_b"][0], 16)
+    assert int(z.view(np.uint16)[1, 0]) == int(gd["zero_bits_b"][0], 16)
+    assert O.mae(w, packed, s, z) == pytest.approx(float(gd["mae_both"][0]), abs=1e-7)
+    # row B alone is exact: every value involved is a dyadic rational
+    wb = b.reshape(1, 16)
+    assert O.mae(wb, *O.quantize_pack(wb, O.ROWWISE)) == 105.0 / 16384.0

@@ -73,7 +73,10 @@ def _brute_quantize(w32, mode, g):
             s16 = 1
         z32 = round_fmt((0 - lo) / s16, "f32")
         z16 = round_fmt(z32, "f16")
-        assert not isinstance(z16, float), "test data must keep z finite"
+        if isinstance(z16, float):  # an fp16 zero beyond 65504: the group is treated as constant
+            s16 = 1
+            z16 = round_fmt(round_fmt(0 - lo, "f32"), "f16")
+        assert not isinstance(z16, float), "test data must keep |min| <= 65504"
         for (n, k), v in zip(grp, vals):
             a = round_fmt(v / s16, "f32")
             t = round_fmt(a + z16, "f32")
@@ -97,6 +100,10 @@ def _tiny_inputs():
     cases.append(("special", w))
     cases.append(("fp16grid", r.standard_normal((2, 64)).astype(np.float16).astype(np.float32)))
     cases.append(("wide", (r.standard_normal((2, 32)) * 300).astype(np.float32)))
+    # groups whose range is tiny next to their offset: the fp16 zero -min/s would overflow
+    n = np.float32(1.0) + np.float32(1e-4) * r.random((2, 32), dtype=np.float32)
+    n[1, :16] = np.float32(-1000.0) - np.float32(0.01) * r.random(16, dtype=np.float32)
+    cases.append(("narrow", n))
     return cases
 
 
@@ -231,3 +238,32 @@ def test_int_zero_invariants(mode, g):
     # every in-range weight is within half a step of its dequantized value (up to rounding)
     sx = _expand(s, *w.shape)
     assert np.all(np.abs(deq - w) <= 0.5 * sx * (1 + 1e-3) + 1e-7)
+
+
+def test_zero_overflow_group():
+    """fp32 [1.0, 1.0001]: s = fp16(1e-4 / 15) is an fp16 subnormal and -min/s ~ -1.5e5 is
+    beyond fp16, so the group is quantized as a constant group: s = 1, z = -1, every code 0
+    and the dequantized values exactly 1.0 (finite).  Only fp32 weights reach this: an fp16
+    or bf16 group's range is at least one unit of its min's last place, so |min| / range is
+    at most 2^11 and -min/s stays below 15 * 2^11 < 65504."""
+    w = np.array([[1.0, 1.0001] + [1.00005] * 14], dtype=np.float32)
+    for mode, g in [(O.ROWWISE, None), (O.GROUPWISE, 16), (O.GLOBAL, None)]:
+        packed, s, z = O.quantize_pack(w, mode, g)
+        assert int(s.view(np.uint16)[0, 0]) == 0x3C00
+        assert int(z.view(np.uint16)[0, 0]) == 0xBC00  # -1.0
+        assert np.all(O.unpack(packed) == 0)
+        assert np.all(O.dequantize_f32(packed, s, z, 16) == 1.0)
+
+
+def test_zero_overflow_bound():
+    """The fallback applies exactly when fp16(-min / s) overflows: a group with a finite
+    zero point just below 65504 keeps its min-max scale."""
+    lo = np.float32(-1.0)
+    # s = 2^-14 (fp16 normal): -lo / s = 16384, finite; the group keeps s
+    w = np.array([[lo, lo + np.float32(15 * 2.0 ** -14)]], dtype=np.float32)
+    _, s, z = O.quantize_pack(np.repeat(w, 8, axis=1), O.ROWWISE)
+    assert float(s[0, 0]) == 2.0 ** -14 and float(z[0, 0]) == 16384.0
+    # s = 2^-17 (fp16 subnormal): -lo / s = 131072 overflows fp16; s falls back to 1
+    w = np.array([[lo, lo + np.float32(15 * 2.0 ** -17)]], dtype=np.float32)
+    _, s, z = O.quantize_pack(np.repeat(w, 8, axis=1), O.ROWWISE)
+    assert float(s[0, 0]) == 1.0 and float(z[0, 0]) == 1.0
