@@ -14,6 +14,7 @@ from .ops import (  # noqa: F401
     kernel_for,
     meta_shape,
     mm,
+    mm_plan,
     mm_split,
     mode_id,
     quantize_fused,

@@ -26,7 +26,7 @@ ZERO_FP16, ZERO_INT = 0, 1
 # every entry point declared in include/w4a16.h
 EXPORTS = (
     "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize", "w4a16_mm",
-    "w4a16_mm_out", "w4a16_mm_kernel", "w4_serial_layout", "w4_serial_parse", "w4_status_string", "w4_last_error",
+    "w4a16_mm_out", "w4a16_mm_kernel", "w4a16_mm_plan", "w4_serial_layout", "w4_serial_parse", "w4_status_string", "w4_last_error",
     "w4_version",
 )
 
@@ -37,6 +37,10 @@ class W4Desc(ctypes.Structure):
 
 class W4OutSeg(ctypes.Structure):
     _fields_ = [("Y", ctypes.c_void_p), ("cols", ctypes.c_int64), ("ld", ctypes.c_int64)]
+
+
+class W4MmPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("lds_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class W4SerialHeader(ctypes.Structure):
@@ -83,6 +87,7 @@ def lib() -> ctypes.CDLL:
     L.w4_serial_parse.argtypes = [vp, sz, pdesc, ctypes.POINTER(ctypes.c_int)]
     L.w4a16_mm_kernel.argtypes = [i64, pdesc, i32]
     L.w4a16_mm_kernel.restype = ctypes.c_char_p
+    L.w4a16_mm_plan.argtypes = [i64, pdesc, i32, sz, ctypes.POINTER(W4MmPlan)]
     L.w4_status_string.argtypes = [i32]
     L.w4_status_string.restype = ctypes.c_char_p
     L.w4_last_error.argtypes = []
@@ -90,7 +95,7 @@ def lib() -> ctypes.CDLL:
     L.w4_version.argtypes = []
     L.w4_version.restype = ctypes.c_char_p
     for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize",
-                 "w4a16_mm", "w4a16_mm_out", "w4_serial_layout", "w4_serial_parse"):
+                 "w4a16_mm", "w4a16_mm_out", "w4a16_mm_plan", "w4_serial_layout", "w4_serial_parse"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -64,21 +64,20 @@ int64_t pairs_of(const w4_desc* d) {
 }
 
 w4::DeviceCaps device_caps() {
-  // queried once per process (one device type); defaults are MI355X's
+  // queried once per process (one device type); without a device (host-only queries on a
+  // machine with no GPU) the figures are MI355X's: 160 KB of LDS per workgroup, 256 CUs
   static std::atomic<long long> lds{-1}, cus{-1};
   if (lds.load() < 0) {
     int dev = 0, bytes = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-      bytes = 64 * 1024;
+        hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes <= 0)
+      bytes = 160 * 1024;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cus.store(n);
     lds.store(bytes);
   }
   return w4::DeviceCaps{(size_t)lds.load(), (int)cus.load()};
 }
-
-size_t device_lds_limit() { return device_caps().lds; }
 
 int launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -164,12 +163,15 @@ w4::MmArgs make_args(const uint16_t* A, int64_t M, const int32_t* packed, const 
 
 int run_mm(const w4::MmArgs& a, void* ws, size_t ws_bytes, void* stream) {
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (w4::gemv_supported(a, device_caps())) return launched(w4::launch_gemv(a, device_caps(), st), "gemv");
-  if (w4::gemm_lds_bytes(a, device_caps()) > device_lds_limit())
-    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", w4::gemm_lds_bytes(a, device_caps()),
-                device_lds_limit());
+  const w4::DeviceCaps caps = device_caps();
+  if (w4::gemv_supported(a, caps)) return launched(w4::launch_gemv(a, caps, st), "gemv");
+  const size_t wsb = ws != nullptr ? ws_bytes : 0;
+  // the footprint of the plan this call launches (split or not, given its workspace)
+  const size_t lds = w4::gemm_lds_bytes(a, caps, wsb);
+  if (lds > caps.lds)
+    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", lds, caps.lds);
   if (ws != nullptr && !aligned(ws, 16)) return fail(W4_ERR_ALIGN, "workspace must be 16-byte aligned");
-  return launched(w4::launch_gemm(a, device_caps(), ws, ws != nullptr ? ws_bytes : 0, st), "gemm");
+  return launched(w4::launch_gemm(a, caps, ws, wsb, st), "gemm");
 }
 
 }  // namespace
@@ -292,7 +294,31 @@ const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {
   const w4::Epi ep = {};
   const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, ep);
   if (w4::gemv_supported(a, device_caps())) return w4::gemv_name(a);
-  return w4::gemm_name(a, device_caps(), true);
+  return w4::gemm_name(a, device_caps(), SIZE_MAX);
+}
+
+int w4a16_mm_plan(int64_t M, const w4_desc* desc, int transposed, size_t ws_bytes, w4_mm_plan* plan) {
+  if (plan == nullptr) return fail(W4_ERR_INVALID, "plan is NULL");
+  static const uint16_t dummy[8] __attribute__((aligned(16))) = {0};
+  const void* p = dummy;
+  int s = check_mm(static_cast<const uint16_t*>(p), M, static_cast<const int32_t*>(p), dummy, dummy, desc,
+                   transposed);
+  if (s != W4_OK) return s;
+  *plan = w4_mm_plan{"none", 0, 0};
+  if (M == 0) return ok();
+  const w4::Epi ep = {};
+  const w4::MmArgs a = make_args(dummy, M, static_cast<const int32_t*>(p), dummy, dummy, desc, transposed, ep);
+  const w4::DeviceCaps caps = device_caps();
+  if (w4::gemv_supported(a, caps)) {
+    *plan = w4_mm_plan{w4::gemv_name(a), w4::gemv_lds_bytes(a, caps), 0};
+    return ok();
+  }
+  *plan = w4_mm_plan{w4::gemm_name(a, caps, ws_bytes), w4::gemm_lds_bytes(a, caps, ws_bytes),
+                     w4::gemm_used_workspace_bytes(a, caps, ws_bytes)};
+  if (plan->lds_bytes > caps.lds)
+    return fail(W4_ERR_RESOURCE, "GEMM tile needs %zu bytes of LDS, the device allows %zu", plan->lds_bytes,
+                caps.lds);
+  return ok();
 }
 
 static_assert(sizeof(w4_serial_header) == 128, "the serialized header is 128 bytes");

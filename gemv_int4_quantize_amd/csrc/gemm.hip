@@ -244,21 +244,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       const int n = min(c0 + row, N - 1);
       const int wc = (l0 >> 3) + w0;
       const int32_t* src = packed + (size_t)n * KW + wc;
+      // words past the row (the last step when K % BK != 0) are not read: they multiply
+      // activation columns that are zero, and are set to code 0.  KW % 4 == 0 and wc is a
+      // multiple of W_PER_T, so a 2- or 4-word load is wholly inside or wholly past the row.
       if constexpr (W_PER_T >= 4) {
 #pragma unroll
         for (int h = 0; h < W_PER_T / 4; ++h) {
-          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + h);
+          const u32x4 v = wc + 4 * h < KW ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + h)
+                                          : u32x4{0u, 0u, 0u, 0u};
           R.w[4 * h] = v[0]; R.w[4 * h + 1] = v[1]; R.w[4 * h + 2] = v[2]; R.w[4 * h + 3] = v[3];
         }
       } else if constexpr (W_PER_T == 2) {
-        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+        const u32x2 v = wc < KW ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src)) : u32x2{0u, 0u};
         R.w[0] = v[0]; R.w[1] = v[1];
       } else {
-        R.w[0] = (uint32_t)__builtin_nontemporal_load(src);
+        R.w[0] = wc < KW ? (uint32_t)__builtin_nontemporal_load(src) : 0u;
       }
 #pragma unroll
       for (int i = 0; i < MPT; ++i) {
-        const size_t mi = meta_index(n, wc + i);
+        const size_t mi = meta_index(n, min(wc + i, KW - 1));
         R.s[i] = scales[mi];
         R.z[i] = zeros[mi];
       }
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
       for (int i = 0; i < A_UNITS; ++i) {
         const int u = tid + i * T;
         const int row = u / SLOTS, slot = u % SLOTS;
-        const bool in = TRANS ? (KB + kt) * BK + slot * 8 < L : true;
+        const bool in = (KB + kt) * BK + slot * 8 < L;  // columns past the contraction read as zero
         *reinterpret_cast<u32x4*>(as + row * LR + slot * 8) = in ? R.a[i] : u32x4{0u, 0u, 0u, 0u};
       }
     }
@@ -876,6 +880,14 @@ hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st)
   return run_cfg(a, p.cfg, GemmPart{p.tail_splits, tn - p.tail_cols, p.tail_cols}, part, st);
 }
 
+// The plan a launch with a workspace of ws_bytes runs: the split plan when it fits the
+// workspace, else the unsplit one.
+Plan launched_plan(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  Plan p = pick_plan(a, caps, ws_bytes > 0);
+  if ((p.splits > 1 || p.tail_cols > 0) && split_bytes(a, p) > ws_bytes) p = pick_plan(a, caps, false);
+  return p;
+}
+
 }  // namespace
 
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t c_lo, int64_t pw, const Epi& ep,
@@ -885,9 +897,9 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_
   return hipGetLastError();
 }
 
-const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspace) {
+const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
   static thread_local char buf[64];
-  const Plan p = pick_plan(a, caps, with_workspace);
+  const Plan p = launched_plan(a, caps, ws_bytes);
   const Cfg& c = kCfgs[p.cfg];
   if (p.tail_cols > 0) {
     snprintf(buf, sizeof(buf), "%s_tail%d_splitk%d", c.name, p.tail_cols, p.tail_splits);
@@ -898,8 +910,12 @@ const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspa
   return buf;
 }
 
-size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps) {
-  return lds_bytes(kCfgs[pick_plan(a, caps, false).cfg]);
+size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  return lds_bytes(kCfgs[launched_plan(a, caps, ws_bytes).cfg]);
+}
+
+size_t gemm_used_workspace_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  return split_bytes(a, launched_plan(a, caps, ws_bytes));
 }
 
 size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps) {
@@ -907,9 +923,7 @@ size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps) {
 }
 
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st) {
-  Plan p = pick_plan(a, caps, ws != nullptr);
-  if ((p.splits > 1 || p.tail_cols > 0) && split_bytes(a, p) > ws_bytes) p = pick_plan(a, caps, false);
-  return run_plan(a, p, static_cast<float*>(ws), st);
+  return run_plan(a, launched_plan(a, caps, ws != nullptr ? ws_bytes : 0), static_cast<float*>(ws), st);
 }
 
 }  // namespace w4

@@ -416,6 +416,8 @@ bool gemv_supported(const MmArgs& a, const DeviceCaps& caps) {
   return plan(a, caps).phase_iters >= 1;
 }
 
+size_t gemv_lds_bytes(const MmArgs& a, const DeviceCaps& caps) { return plan(a, caps).lds; }
+
 const char* gemv_name(const MmArgs& a) {
   static const char* names[] = {"gemv_m1", "gemv_m2", "gemv_m3", "gemv_m4"};
   return names[a.M - 1];

@@ -55,14 +55,17 @@ struct DeviceCaps {
 // (LDS footprint), so the caller can fall back to the GEMM.
 bool gemv_supported(const MmArgs& a, const DeviceCaps& caps);
 const char* gemv_name(const MmArgs& a);
+size_t gemv_lds_bytes(const MmArgs& a, const DeviceCaps& caps);
 hipError_t launch_gemv(const MmArgs& a, const DeviceCaps& caps, hipStream_t st);
 
-// GEMM: kernel name (with a split-K suffix when a workspace would be used), LDS
-// footprint, the workspace the split-K plan wants (0 if none) and the launch, which
-// splits the contraction only when `ws` holds at least the planned bytes.
-const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, bool with_workspace);
-size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps);
+// GEMM: the workspace the split-K plan wants (0 if none), and for a launch given a
+// workspace of ws_bytes (0: none) the plan it runs -- split only when ws_bytes holds the
+// split plan's bytes: its kernel name (with a split-K or split-tail suffix), the LDS bytes
+// of its tile and the workspace bytes it uses.  launch_gemm runs that same plan.
 size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps);
+const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes);
+size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes);
+size_t gemm_used_workspace_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes);
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st);
 
 // The part of a GEMM one launch covers: output column tiles [ct0, ct0 + nct) (nct = 0:

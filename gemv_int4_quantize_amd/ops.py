@@ -312,3 +312,14 @@ def kernel_for(M: int, N: int, K: int, mode="groupwise", group: int | None = 128
     desc = W4Desc(N, K, m, int(group) if m == MODE_GROUPWISE else 0)
     r = lib().w4a16_mm_kernel(M, ctypes.byref(desc), 1 if transposed else 0)
     return r.decode() if r is not None else None
+
+
+def mm_plan(M: int, N: int, K: int, mode="groupwise", group: int | None = 128, transposed=False,
+            ws_bytes: int = 0) -> dict:
+    """The launch a matmul makes with a workspace of ``ws_bytes`` (host-side query):
+    ``{"kernel", "lds_bytes", "workspace_bytes"}``; raises W4Error as the matmul would."""
+    m = mode_id(mode)
+    desc = W4Desc(N, K, m, int(group) if m == MODE_GROUPWISE else 0)
+    out = _lib.W4MmPlan()
+    _lib.check(lib().w4a16_mm_plan(M, ctypes.byref(desc), 1 if transposed else 0, ws_bytes, ctypes.byref(out)))
+    return {"kernel": out.kernel.decode(), "lds_bytes": int(out.lds_bytes), "workspace_bytes": int(out.workspace_bytes)}

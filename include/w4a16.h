@@ -25,8 +25,10 @@
  * Arithmetic:
  *   s = fp16_rne((max - min) / 15) per group, replaced by 1 when it is 0 or not
  *   finite; z = fp16_rne((0 - min) / s); q = clamp(rint(w / s + z), 0, 15), all
- *   in IEEE fp32.  The matmul weight operand is bf16_rne((q - z) * s) and products
- *   accumulate in fp32.
+ *   in IEEE fp32.  When that z is not finite (a group whose range is below
+ *   15 |min| / 65504, which only fp32 weights reach), the group is quantized as
+ *   a constant one: s = 1 and z = fp16_rne(0 - min).  The matmul weight
+ *   operand is bf16_rne((q - z) * s) and products accumulate in fp32.
  *
  * Ownership and execution: every pointer is a device pointer owned by the caller
  * (except the descriptor and the host out-parameters).  The library never
@@ -173,6 +175,23 @@ int w4a16_mm_out(const void* A, int a_dtype, int64_t M, const int32_t* packed,
  * "gemm_nt_256x128", "gemm_t_256x256_splitk4", ...) given the workspace
  * w4_workspace_bytes reports, or NULL when they are invalid.  Host only. */
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed);
+
+/* The launch w4a16_mm / w4a16_mm_out makes for these arguments when given a
+ * workspace of ws_bytes (0: none): `kernel` is its kernel name, as
+ * w4a16_mm_kernel reports it for the full workspace ("none" for M == 0; the
+ * string lives in storage of the calling thread until its next call),
+ * `lds_bytes` the LDS one workgroup of that kernel uses, and `workspace_bytes`
+ * the part of the workspace it writes (0 when the contraction is not split;
+ * a workspace smaller than the split plan needs is not used).  Returns
+ * W4_ERR_RESOURCE when lds_bytes is above the device's limit (the matmul
+ * would fail the same way), else the argument checks of w4a16_mm without its
+ * pointers.  Host only. */
+typedef struct {
+  const char* kernel;
+  size_t lds_bytes;
+  size_t workspace_bytes;
+} w4_mm_plan;
+int w4a16_mm_plan(int64_t M, const w4_desc* desc, int transposed, size_t ws_bytes, w4_mm_plan* plan);
 
 /* Serialized packed weight: this 128-byte little-endian header, then the packed
  * words [N][K/8] int32, the scales and the zeros (fp16 bits, w4_meta_pairs each),

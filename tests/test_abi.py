@@ -180,3 +180,55 @@ def test_mm_out_validation_before_launch():
     # M == 0: structure still checked, pointers never touched
     assert call([(None, 64, 64)], 1, M=0) == _lib.W4_OK
     assert call([(None, 32, 32)], 1, M=0) == _lib.W4_ERR_INVALID
+
+
+def test_mm_plan_follows_the_launch():
+    """w4a16_mm_plan reports the launch a matmul makes for a given workspace: the split
+    plan and its bytes only when the workspace holds them, the unsplit tile otherwise."""
+    L = _lib.lib()
+    for t, name in ((False, "gemm_nt_"), (True, "gemm_t_")):
+        d = _lib.W4Desc(4096, 4096, _lib.MODE_GROUPWISE, 128)
+        need = ctypes.c_size_t(0)
+        assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM_T if t else _lib.OP_MM, 64, ctypes.byref(need)) == 0
+        full = w4.mm_plan(64, 4096, 4096, "groupwise", 128, transposed=t, ws_bytes=need.value)
+        assert full["kernel"] == w4.kernel_for(64, 4096, 4096, "groupwise", 128, transposed=t)
+        assert "_splitk" in full["kernel"] and full["workspace_bytes"] == need.value
+        for ws in (0, need.value - 1):
+            p = w4.mm_plan(64, 4096, 4096, "groupwise", 128, transposed=t, ws_bytes=ws)
+            assert p["kernel"].startswith(name) and "_splitk" not in p["kernel"] and p["workspace_bytes"] == 0
+            assert 0 < p["lds_bytes"] <= 160 * 1024
+    g = w4.mm_plan(4, 16384, 16384, "groupwise", 128)
+    assert g["kernel"] == "gemv_m4" and g["workspace_bytes"] == 0 and 0 < g["lds_bytes"] <= 160 * 1024
+    assert w4.mm_plan(0, 64, 64, "rowwise", None)["kernel"] == "none"
+    with pytest.raises(w4.W4Error):
+        w4.mm_plan(4, 64, 40, "rowwise", None)
+
+
+def _forced_plan(cfg, M, N, K, transposed, ws):
+    """The plan under W4A16_GEMM_CFG=cfg, queried in a fresh process (the override is read once)."""
+    import json
+    import subprocess
+    import sys
+    code = ("import json, sys; sys.path.insert(0, %r); import gemv_int4_quantize_amd as w4; "
+            "print(json.dumps(w4.mm_plan(%d, %d, %d, 'rowwise', None, %r, %d)))"
+            % (os.path.dirname(os.path.dirname(os.path.abspath(__file__))), M, N, K, transposed, ws))
+    env = dict(os.environ, W4A16_GEMM_CFG=str(cfg))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+@pytest.mark.parametrize("cfg,name,transposed,N,K", [(0, "gemm_t_256x256", True, 4096, 4096),
+                                                     (1, "gemm_t_256x128", True, 4096, 4096),
+                                                     (5, "gemm_nt_lds_256x256", False, 64, (1 << 21) + 64)])
+def test_forced_tile_footprint(cfg, name, transposed, N, K):
+    """A tile forced through W4A16_GEMM_CFG is the one reported and launched, split or not,
+    with its LDS footprint: two stages of (BM + BN) rows of BK + 8 bf16 values.  (The
+    non-transposed LDS tile serves contractions longer than 2^21 only.)"""
+    bm, bn = (int(v) for v in name.rsplit("_", 1)[1].split("x"))
+    want = 2 * (bm + bn) * (64 + 8) * 2
+    for M, ws in ((64, 1 << 30), (64, 0), (4096, 1 << 30)):
+        p = _forced_plan(cfg, M, N, K, transposed, ws)
+        assert p["kernel"].startswith(name), p
+        assert p["lds_bytes"] == want, p
+        assert (p["workspace_bytes"] > 0) == ("_splitk" in p["kernel"]), p
