@@ -7,8 +7,8 @@ import torch
 import gemv_int4_quantize_amd as w4
 import oracle as O
 import synth
-from gpu_helpers import (DEV, ELEM_ATOL, ELEM_RTOL, assert_mm_close, dev_bf16, dev_f32, dev_weight, host,
-                         oracle_rows_global)
+from gpu_helpers import (DEV, ELEM_ATOL, ELEM_RTOL, assert_mm_close, assert_quant_equal, dev_bf16, dev_f32,
+                         dev_weight, host, oracle_rows_global)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,7 +118,7 @@ def test_single_matmul_case():
     qw = w4.quantize_pack(dev_weight(w, "f32"), "groupwise", 128)
     y = w4.mm(dev_bf16(x), qw)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(qw.packed), ref[0])
+    assert_quant_equal(qw, *ref, what="single matmul")
     assert_mm_close(host(y), O.matmul(x, *ref, 2048), "single matmul")
 
 
@@ -246,7 +246,7 @@ def test_split_tail_gemm(ci):
         # the bf16 output is the fp32 epilogue value of the same plan, rounded once
         y32 = w4.mm(ad, qw, transposed=t, bias=bd)
         assert torch.equal(y1, y32.to(torch.bfloat16))
-    ms = np.sort(np.random.default_rng(ci).choice(M, 16, replace=False))
+    ms = _edge_idx(M, np.random.default_rng(ci), 16)
     msd = torch.from_numpy(ms).to(DEV)
     want = O.bf16_bits_to_f64(a[ms]) @ (wdq if t else wdq.T)
     if epi:
@@ -269,17 +269,32 @@ DECODE_SHAPES = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (204
 
 @pytest.mark.parametrize("si", range(len(DECODE_SHAPES)), ids=[f"{n}x{k}" for n, k in DECODE_SHAPES])
 def test_decode_gemv_full(si):
-    """Decode batched GEMV, Llama-2-7B-like layers, g=128, M = 1..4: sampled rows of Y."""
+    """Decode batched GEMV, Llama-2-7B-like layers, g=128, M = 1..4, at full size: the
+    packed codes, scales and zeros bit-exact with the oracle, and every output of Y."""
     N, K = DECODE_SHAPES[si]
     print(f"[case] decode full N={N} K={K}", flush=True)
     w = synth.weight(2, si, N, K, "bf16")
     qw = w4.quantize_pack(dev_weight(w, "bf16"), "groupwise", 128)
-    rows = np.sort(np.random.default_rng(si).choice(N, 48, replace=False))
-    ref = O.quantize_pack(O.to_f32(w[rows], "bf16"), O.GROUPWISE, 128)
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), O.GROUPWISE, 128)
+    del w
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"decode {N}x{K}")
+    wdq = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref, K))  # the oracle's weight operand [N][K]
     for M in (1, 2, 3, 4):
         x = synth.activations_bf16(2, si * 10 + M, M, K)
         y = host(w4.mm(dev_bf16(x), qw))
-        assert_mm_close(y[:, rows], O.matmul(x, *ref, K), f"decode {N}x{K} M={M}")
+        assert_mm_close(y, O.bf16_bits_to_f64(x) @ wdq.T, f"decode {N}x{K} M={M}")
+
+
+def _edge_idx(n, rng, k):
+    """k random indices below n plus the tile edges every planner route has: the first and
+    last index, and both sides of each multiple of 32, 64, 128 and 256 near the ends."""
+    edges = {0, 1, n - 2, n - 1}
+    for t in (32, 64, 128, 256):
+        for b in (t, 2 * t, (n // t) * t, (n // t - 1) * t):
+            edges.update((b - 1, b))
+    pick = set(rng.choice(n, min(n, k), replace=False).tolist())
+    return np.array(sorted(i for i in edges | pick if 0 <= i < n))
 
 
 PREFILL_SHAPES = [(2048, 2048), (8192, 2048), (2048, 8192), (512, 2048), (128256, 2048)]
@@ -293,7 +308,7 @@ def test_prefill_gemm_full(si):
     w32 = O.to_f32(w, "bf16")
     wd = dev_weight(w, "bf16")
     bias = synth.bias_f32(3, si, N)
-    rows = np.sort(np.random.default_rng(100 + si).choice(N, min(N, 40), replace=False))
+    rows = _edge_idx(N, np.random.default_rng(100 + si), 40)
     for mode, g in [("global", None), ("rowwise", None), ("groupwise", 64)]:
         print(f"[case] prefill full N={N} K={K} mode={mode}", flush=True)
         qw = w4.quantize_pack(wd, mode, g)
@@ -304,7 +319,7 @@ def test_prefill_gemm_full(si):
         for M in (128, 512, 2048):
             x = synth.activations_bf16(3, si * 10 + M, M, K)
             y = w4.mm(dev_bf16(x), qw, bias=dev_f32(bias))
-            ms = np.sort(np.random.default_rng(M).choice(M, 24, replace=False))
+            ms = _edge_idx(M, np.random.default_rng(M), 24)
             ys = host(y[torch.from_numpy(ms).to(DEV)][:, torch.from_numpy(rows).to(DEV)])
             del y
             assert_mm_close(ys, O.matmul(x[ms], *ref, K, bias=bias[rows]), f"prefill {N}x{K} {mode} M={M}")
@@ -332,9 +347,9 @@ def test_qlora_pair_full(si):
             qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
         ref_full = O.quantize_pack(w32, OMODE[mode], g)
         wdq = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref_full, K))  # oracle weight operand [N][K]
-        rows = np.sort(np.random.default_rng(200 + si).choice(N, 32, replace=False))
+        rows = _edge_idx(N, np.random.default_rng(200 + si), 32)
         for M in (1024, 2048, 4096):
-            ms = np.sort(np.random.default_rng(M + si).choice(M, 12, replace=False))
+            ms = _edge_idx(M, np.random.default_rng(M + si), 12)
             msd = torch.from_numpy(ms).to(DEV)
             x = synth.activations_bf16(4, si * 10 + M, M, K)
             y = w4.mm(dev_bf16(x), qw)

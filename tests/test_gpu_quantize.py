@@ -7,7 +7,7 @@ import torch
 import gemv_int4_quantize_amd as w4
 import oracle as O
 import synth
-from gpu_helpers import (DEV, assert_quant_equal, dev_weight, host, host_bits16, oracle_rows_global)
+from gpu_helpers import DEV, assert_quant_equal, dev_weight, host, host_bits16
 
 pytestmark = pytest.mark.gpu
 
@@ -63,28 +63,23 @@ def test_quantize_odd_shapes(N, K, mode, g):
 @pytest.mark.parametrize("mode,g", [("global", None), ("rowwise", None), ("groupwise", 16), ("groupwise", 32),
                                     ("groupwise", 64), ("groupwise", 128), ("groupwise", 256), ("groupwise", 512),
                                     ("groupwise", 1024), ("groupwise", 2048)])
-def test_quantize_full_size_sampled(mode, g, full_quant_weight):
-    """fp16 W [128256][2048] with 0.1% outliers: every scale / zero and sampled rows of codes."""
+def test_quantize_full_size(mode, g, full_quant_weight):
+    """fp16 W [128256][2048] with 0.1% outliers: the whole packed tensor and every scale and
+    zero, bit-exact with the oracle on the full tensor."""
     print(f"[case] quantize full 128256x2048 mode={mode} g={g}", flush=True)
-    w, wd, rows = full_quant_weight
-    w32 = O.to_f32(w[rows], "f16")
+    w32, wd = full_quant_weight
     qw = w4.quantize_pack(wd, mode, g)
     torch.cuda.synchronize()
-    if mode == "global":
-        ref = oracle_rows_global(O.to_f32(w, "f16"), rows)
-    else:
-        ref = O.quantize_pack(w32, OMODE[mode], g)
-    assert_quant_equal(qw, *ref, rows=rows, what=f"full {mode} {g}")
+    ref = O.quantize_pack(w32, OMODE[mode], g)
+    assert_quant_equal(qw, *ref, what=f"full {mode} {g}")
 
 
 @pytest.fixture(scope="module")
 def full_quant_weight():
     N, K = 128256, 2048
     w = synth.weight_with_outliers(5, 0, N, K)
-    rows = np.sort(np.random.default_rng(55).choice(N, 96, replace=False))
-    rows = np.concatenate([[0, N - 1], rows])
     wd = dev_weight(w, "f16")
-    yield w, wd, rows
+    yield O.to_f32(w, "f16"), wd
     del wd
     torch.cuda.empty_cache()
 
@@ -182,3 +177,24 @@ def test_quantize_exact_ties(dtype, mode, g, zero):
     qw = w4.quantize_pack(dev_weight(w, dtype), mode, g, zero=zero)
     torch.cuda.synchronize()
     assert_quant_equal(qw, *ref, what=f"ties {dtype} {mode} {g} {zero}")
+
+
+@pytest.mark.parametrize("mode,g", [("rowwise", None), ("groupwise", 16), ("groupwise", 128), ("global", None)])
+def test_quantize_zero_overflow(mode, g):
+    """fp32 groups whose fp16 zero point would overflow (range below 15 |min| / 65504, e.g.
+    [1.0, 1.0001]) are quantized as constant groups (s = 1, z = fp16(0 - min)), bit-exact
+    with the oracle, and dequantize to finite values."""
+    print(f"[case] quantize zero overflow mode={mode} g={g}", flush=True)
+    N, K = 12, 1024
+    r = np.random.default_rng(77)
+    w = (np.float32(1.0) + np.float32(1e-4) * r.random((N, K), dtype=np.float32)).astype(np.float32)
+    w[:, 0], w[:, 1] = 1.0, 1.0001
+    w[3, :] = np.float32(-1000.0) - np.float32(0.01) * r.random(K, dtype=np.float32)
+    w[5, :] = (r.standard_normal(K) * 0.02).astype(np.float32)   # an ordinary row among them
+    ref = O.quantize_pack(w, OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "f32"), mode, g)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, *ref, what=f"zero overflow {mode} {g}")
+    d = host(w4.dequantize(qw, torch.float32))
+    assert np.all(np.isfinite(d))
+    np.testing.assert_array_equal(d.view(np.uint32), O.dequantize_f32(*ref, K).view(np.uint32))
