@@ -7,9 +7,13 @@ gradient is produced for it (nor for the base bias).  Source: "Re-write HQQ Fuse
 Gemm Transpose" (pytorch/ao #185), which fine-tunes a frozen 4-bit base with LoRA
 adapters and needs exactly these two products of one packed weight.
 
-The library's matmul accumulates and returns fp32; activations and incoming
-gradients enter it as bf16 (a dtype conversion here is argument marshalling, the
-products themselves run in the gfx950 kernels).
+The library's matmul accumulates and returns fp32.  bf16 and fp16 activations enter
+it as they are (fp16 activations multiply the fp16 weight operand); other dtypes
+are converted to bf16.  The incoming gradient takes the activations' 16-bit dtype
+(fp16 gradients need the caller's loss scaling, as in any fp16 training).  A
+dtype conversion here is argument marshalling; the products run in the gfx950
+kernels.  A bias that requires grad gets the sum of the incoming gradient over
+the rows.
 """
 
 from __future__ import annotations
@@ -20,16 +24,20 @@ from . import ops
 from .ops import QuantizedWeight
 
 
+def _operand(t: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    return (t if t.dtype == dtype else t.to(dtype)).contiguous()
+
+
 class _W4A16Matmul(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x: torch.Tensor, qw: QuantizedWeight, bias: torch.Tensor | None):
         lead = x.shape[:-1]
-        x2 = x.reshape(-1, x.shape[-1])
-        if x2.dtype != torch.bfloat16:
-            x2 = x2.to(torch.bfloat16)
-        y = ops.mm(x2.contiguous(), qw, bias=bias)
+        adt = x.dtype if x.dtype in (torch.bfloat16, torch.float16) else torch.bfloat16
+        y = ops.mm(_operand(x.reshape(-1, x.shape[-1]), adt), qw,
+                   bias=None if bias is None else _operand(bias, torch.float32))
         ctx.qw = qw
         ctx.x_dtype = x.dtype
+        ctx.a_dtype = adt
         ctx.lead = lead
         return y.view(*lead, qw.N)
 
@@ -37,10 +45,11 @@ class _W4A16Matmul(torch.autograd.Function):
     def backward(ctx, gy: torch.Tensor):
         qw: QuantizedWeight = ctx.qw
         g2 = gy.reshape(-1, qw.N)
-        if g2.dtype != torch.bfloat16:
-            g2 = g2.to(torch.bfloat16)
-        dx = ops.mm(g2.contiguous(), qw, transposed=True)
-        return dx.view(*ctx.lead, qw.K).to(ctx.x_dtype), None, None
+        dx = None
+        if ctx.needs_input_grad[0]:
+            dx = ops.mm(_operand(g2, ctx.a_dtype), qw, transposed=True).view(*ctx.lead, qw.K).to(ctx.x_dtype)
+        db = g2.sum(0) if ctx.needs_input_grad[2] else None
+        return dx, None, db
 
 
 def w4a16_linear(x: torch.Tensor, qw: QuantizedWeight, bias: torch.Tensor | None = None) -> torch.Tensor:

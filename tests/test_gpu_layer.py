@@ -40,3 +40,29 @@ def test_layer_forward_backward(mode, g, lead):
     assert_mm_close(host(x.grad).reshape(M, K), O.matmul(gb, *ref, K, transposed=True), f"layer dX {mode}")
     # the base weight is frozen: no tensor of the packed operand takes part in autograd
     assert not any(t.requires_grad for t in (layer.qw.packed, layer.qw.scales, layer.qw.zeros))
+
+
+def test_layer_fp16_and_trainable_bias():
+    """fp16 activations and gradients take the fp16 path (fp16 weight operand) end to end,
+    against the oracle's fp16 matmul; a bias that requires grad gets the row sum of dY."""
+    N, K, M = 520, 1024, 130
+    print("[case] layer fp16", flush=True)
+    wb = synth.weight(713, 0, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(wb, "bf16"), O.GROUPWISE, 64)
+    qw = w4.quantize_pack(dev_weight(wb, "bf16"), "groupwise", 64)
+    x16 = synth.activations_bf16(713, 1, M, K)  # draws; stored below as fp16
+    xf = _bf16_to_f32(x16).astype(np.float16)
+    gf = _bf16_to_f32(synth.activations_bf16(713, 2, M, N, tensor_id=synth.T_DY)).astype(np.float16)
+    bias = torch.from_numpy(synth.bias_f32(713, 3, N)).to(DEV).requires_grad_(True)
+    x = torch.from_numpy(xf).to(DEV).requires_grad_(True)
+    y = w4.w4a16_linear(x, qw, bias)
+    assert y.dtype == torch.float32
+    xb = xf.view(np.uint16)
+    assert_mm_close(host(y.detach()), O.matmul(xb, *ref, K, bias=host(bias.detach()), a_dtype="f16"),
+                    "layer fp16 forward")
+    y.backward(torch.from_numpy(gf.astype(np.float32)).to(DEV))
+    assert x.grad.dtype == torch.float16
+    assert_mm_close(host(x.grad.float()), O.matmul(gf.view(np.uint16), *ref, K, transposed=True, a_dtype="f16"),
+                    "layer fp16 dX (fp16 stored)")
+    want_db = gf.astype(np.float64).sum(0)
+    np.testing.assert_allclose(host(bias.grad).astype(np.float64), want_db, rtol=1e-5, atol=1e-4)
