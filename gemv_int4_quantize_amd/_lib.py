@@ -26,8 +26,8 @@ ZERO_FP16, ZERO_INT = 0, 1
 # every entry point declared in include/w4a16.h
 EXPORTS = (
     "w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize", "w4a16_mm",
-    "w4a16_mm_out", "w4a16_mm_kernel", "w4a16_mm_plan", "w4_serial_layout", "w4_serial_parse", "w4_status_string", "w4_last_error",
-    "w4_version",
+    "w4a16_mm_out", "w4a16_mm_noalloc", "w4a16_mm_kernel", "w4a16_mm_plan", "w4_serial_layout", "w4_serial_parse",
+    "w4_status_string", "w4_last_error", "w4_version",
 )
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
     L.w4_quantize_pack_zp.argtypes = [vp, i32, pdesc, i32, vp, vp, vp, vp, sz, vp]
     L.w4_dequantize.argtypes = [vp, vp, vp, pdesc, vp, i32, vp]
     L.w4a16_mm.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp, sz, vp]
+    L.w4a16_mm_noalloc.argtypes = [vp, i64, vp, vp, vp, pdesc, i32, vp, vp, vp]
     L.w4a16_mm_out.argtypes = [vp, i32, i64, vp, vp, vp, pdesc, i32, vp, i32, ctypes.POINTER(W4OutSeg), i32, vp, sz,
                                vp]
     L.w4_serial_layout.argtypes = [pdesc, i32, ctypes.POINTER(W4SerialHeader)]
@@ -95,7 +96,8 @@ def lib() -> ctypes.CDLL:
     L.w4_version.argtypes = []
     L.w4_version.restype = ctypes.c_char_p
     for name in ("w4_meta_pairs", "w4_workspace_bytes", "w4_quantize_pack", "w4_quantize_pack_zp", "w4_dequantize",
-                 "w4a16_mm", "w4a16_mm_out", "w4a16_mm_plan", "w4_serial_layout", "w4_serial_parse"):
+                 "w4a16_mm", "w4a16_mm_out", "w4a16_mm_noalloc", "w4a16_mm_plan", "w4_serial_layout",
+                 "w4_serial_parse"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

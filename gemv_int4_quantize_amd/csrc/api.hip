@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -174,6 +175,34 @@ int run_mm(const w4::MmArgs& a, void* ws, size_t ws_bytes, void* stream) {
   return launched(w4::launch_gemm(a, caps, ws, wsb, st), "gemm");
 }
 
+// Split-K scratch of w4a16_mm_noalloc, for callers that cannot allocate: a file-scope
+// device array, one copy per GPU, held until the process ends.  Host code uses the
+// address hipGetSymbolAddress returns for the current device, never the array's name.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per device).
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(W4_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4_ERR_UNSUPPORTED, "device %d is past the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(W4_ERR_LAUNCH, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +311,34 @@ int w4a16_mm_out(const void* A, int a_dtype, int64_t M, const int32_t* packed, c
   if (M == 0) return ok();
   return run_mm(make_args(A16, M, packed, scales, zeros, desc, transposed, ep, a_dtype == W4_DT_F16), ws, ws_bytes,
                 stream);
+}
+
+int w4a16_mm_noalloc(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
+                     const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias, float* Y,
+                     void* stream) {
+  int s = check_mm(A, M, packed, scales, zeros, desc, transposed);
+  if (s != W4_OK) return s;
+  if (M == 0) return ok();
+  if (Y == nullptr) return fail(W4_ERR_INVALID, "a required pointer is NULL");
+  const int64_t outc = transposed ? desc->K : desc->N;
+  const w4_out_seg seg = {Y, outc, outc};
+  w4::Epi ep;
+  s = make_epi(desc, transposed, M, bias, W4_DT_F32, &seg, 1, &ep);
+  if (s != W4_OK) return s;
+  const w4::MmArgs a = make_args(A, M, packed, scales, zeros, desc, transposed, ep);
+  const w4::DeviceCaps caps = device_caps();
+  // the plan w4a16_mm runs with the workspace w4_workspace_bytes reports
+  const size_t need = w4::gemv_supported(a, caps) ? 0 : w4::gemm_workspace_bytes(a, caps);
+  if (need > kScratchBytes)
+    return fail(W4_ERR_RESOURCE,
+                "the split-K planes need %zu bytes, the static scratch holds %zu: use w4a16_mm with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    s = scratch_of_current_device(&ws);
+    if (s != W4_OK) return s;
+  }
+  return run_mm(a, ws, need, stream);
 }
 
 const char* w4a16_mm_kernel(int64_t M, const w4_desc* desc, int transposed) {

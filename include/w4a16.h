@@ -142,6 +142,21 @@ int w4a16_mm(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t
              const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias,
              float* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* w4a16_mm for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid it): the same operands, plan and results
+ * as w4a16_mm given the workspace w4_workspace_bytes reports, with the split-K
+ * partial planes in a static device scratch of the library (64 MiB per GPU,
+ * held until the process ends) instead of a caller workspace.  A plan whose
+ * planes need more returns W4_ERR_RESOURCE before anything is enqueued (call
+ * w4a16_mm with a workspace then).  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (concurrent streams, or threads) race,
+ * so serialize them.  Each plane is written whole before it is read, so nothing
+ * carries over from the previous call.  The library does not allocate, free or
+ * synchronize here either. */
+int w4a16_mm_noalloc(const uint16_t* A, int64_t M, const int32_t* packed, const uint16_t* scales,
+                     const uint16_t* zeros, const w4_desc* desc, int transposed, const float* bias,
+                     float* Y, void* stream);
+
 /* One output segment of w4a16_mm_out: it receives the next `cols` output columns
  * (segments cover the output columns in order), column j of the segment at row m
  * being Y[m * ld + j] in the call's out_dtype.  Y device pointer, ld >= cols. */
