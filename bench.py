@@ -23,7 +23,11 @@ Also reported in the same JSON line (context, not `value`):
             TFLOP/s = 2MNK / kernel time, fraction of the 2.5 PFLOP/s bf16 peak.
   quantize  fp16 W [128256][2048] ~ N(0,0.02) with 0.1% outliers ~ N(0,0.5), ten
             modes: packed GB/s, MAE of the fp32 dequantization, compression ratio.
-  cpu_baseline  the CPU oracle timed on a bounded sample of the GEMV sweep.
+  single_matmul the single-matmul workload (X [4][2048], W fp32 2048x2048, g=128): GPU
+            time per call and the host's enqueue cost per call.
+  midm      M in {8, 16, 32, 64, 100} at the decode shapes, both directions, TFLOP/s.
+  cpu_baseline  the CPU oracle timed on a bounded sample of the GEMV sweep (matmul), and its
+            quantizer on rows of the quantize workload; host CPU model and threads.
 
 Timing: the GPU is parked on a spin kernel while the host enqueues the whole
 batch, so the two HIP events around the timed part measure back-to-back GPU
@@ -132,6 +136,29 @@ def clone_qw(w4, qw):
     return w4.QuantizedWeight(qw.packed.clone(), qw.scales.clone(), qw.zeros.clone(), qw.N, qw.K, qw.mode, qw.group)
 
 
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache (last-level cache)
+
+
+def weight_pool(w4, qw, pool_bytes: int = POOL_BYTES):
+    """Copies of a packed weight that together exceed the last-level cache several times, so a
+    launch rotating through them finds its weight in HBM (a single copy when it is already
+    larger than the cache)."""
+    nb = qw.packed.numel() * 4 + 2 * (qw.scales.numel() + qw.zeros.numel()) * 2
+    n = 1 if nb >= MALL_BYTES else max(2, math.ceil(pool_bytes / nb))
+    return [qw] + [clone_qw(w4, qw) for _ in range(n - 1)]
+
+
+def rotating(pool):
+    """A callable returning the pool's weights in turn."""
+    ctr = [0]
+
+    def nxt():
+        q = pool[ctr[0] % len(pool)]
+        ctr[0] += 1
+        return q
+    return nxt
+
+
 def dev_bf16(torch, bits):
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
@@ -238,13 +265,15 @@ def bench_gemm(torch, w4, synth, reps: int):
             wd = dev_bf16(torch, synth.weight(4, si, N, K, "bf16"))
         for mode, g in [("rowwise", None), ("groupwise", 64)]:
             qw = w4.quantize_fused(parts, mode, g) if parts is not None else w4.quantize_pack(wd, mode, g)
+            pool = weight_pool(w4, qw)
+            nxt = rotating(pool)
             for M in QLORA_M:
                 x = dev_bf16(torch, synth.activations_bf16(4, si * 10 + M, M, K))
                 dy = dev_bf16(torch, synth.activations_bf16(4, si * 10 + M, M, N, tensor_id=synth.T_DY))
                 y = torch.empty((M, N), dtype=torch.float32, device="cuda")
                 dx = torch.empty((M, K), dtype=torch.float32, device="cuda")
-                t_nt = timed(torch, [lambda: w4.mm(x, qw, out=y)] * reps) / reps * 1e-3
-                t_t = timed(torch, [lambda: w4.mm(dy, qw, transposed=True, out=dx)] * reps) / reps * 1e-3
+                t_nt = timed(torch, [lambda: w4.mm(x, nxt(), out=y)] * reps) / reps * 1e-3
+                t_t = timed(torch, [lambda: w4.mm(dy, nxt(), transposed=True, out=dx)] * reps) / reps * 1e-3
                 fl = 2.0 * M * N * K
                 pts.append({"M": M, "N": N, "K": K, "mode": mode if g is None else f"g{g}",
                             "nt_tflops": round(fl / t_nt / 1e12, 1), "t_tflops": round(fl / t_t / 1e12, 1),
@@ -258,18 +287,35 @@ def bench_gemm(torch, w4, synth, reps: int):
                     # (torch / hipBLASLt); also the two bf16 matmuls alone, as if W were stored in bf16
                     F = torch.nn.functional
                     wd16 = w4.dequantize(qw, torch.bfloat16)
-                    fused = [lambda: w4.mm(x, qw, out=y), lambda: w4.mm(dy, qw, transposed=True, out=dx)]
-                    ref = [lambda: w4.dequantize(qw, torch.bfloat16), lambda: F.linear(x, wd16),
-                           lambda: torch.mm(dy, wd16)]
-                    dense = [lambda: F.linear(x, wd16), lambda: torch.mm(dy, wd16)]
+                    dense_pool = [wd16] + [wd16.clone() for _ in range(max(1, math.ceil(POOL_BYTES / (
+                        wd16.numel() * 2))) - 1)] if wd16.numel() * 2 < MALL_BYTES else [wd16]
+                    dctr = [0]
+
+                    def fused_pair():
+                        q = nxt()
+                        w4.mm(x, q, out=y)
+                        w4.mm(dy, q, transposed=True, out=dx)
+
+                    def ref_step():
+                        # the page's reference path: dequantize the frozen weight, then two bf16 matmuls
+                        wd = w4.dequantize(nxt(), torch.bfloat16)
+                        F.linear(x, wd)
+                        torch.mm(dy, wd)
+
+                    def dense_step():
+                        wd = dense_pool[dctr[0] % len(dense_pool)]
+                        dctr[0] += 1
+                        F.linear(x, wd)
+                        torch.mm(dy, wd)
+                    fused, ref, dense = [fused_pair], [ref_step], [dense_step]
                     t_f = timed(torch, fused * reps) / reps * 1e-3
                     t_r = timed(torch, ref * reps) / reps * 1e-3
                     t_d = timed(torch, dense * reps) / reps * 1e-3
                     layer.append({"M": M, "N": N, "K": K, "fused_us": round(t_f * 1e6, 1),
                                   "dequant_ref_us": round(t_r * 1e6, 1), "dense_bf16_us": round(t_d * 1e6, 1)})
-                    del wd16
+                    del wd16, dense_pool
                 del x, dy, y, dx
-            del qw
+            del qw, pool, nxt
         torch.cuda.empty_cache()
     fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
     t_nt = sum(p["nt_us"] for p in pts) * 1e-6
@@ -309,15 +355,17 @@ def bench_prefill(torch, w4, synth, reps: int):
         bias = torch.from_numpy(synth.bias_f32(3, si, N)).cuda()
         for mode, g in [("global", None), ("rowwise", None), ("groupwise", 64)]:
             qw = w4.quantize_pack(wd, mode, g)
+            pool = weight_pool(w4, qw)
+            nxt = rotating(pool)
             for M in PREFILL_M:
                 x = dev_bf16(torch, synth.activations_bf16(3, si * 10 + M, M, K))
                 y = torch.empty((M, N), dtype=torch.float32, device="cuda")
-                t = timed(torch, [lambda: w4.mm(x, qw, bias=bias, out=y)] * reps) / reps * 1e-3
+                t = timed(torch, [lambda: w4.mm(x, nxt(), bias=bias, out=y)] * reps) / reps * 1e-3
                 fl = 2.0 * M * N * K
                 pts.append({"M": M, "N": N, "K": K, "mode": mode if g is None else f"g{g}", "us": round(t * 1e6, 1),
                             "tflops": round(fl / t / 1e12, 1), "kernel": w4.kernel_for(M, N, K, mode, g)})
                 del x, y
-            del qw
+            del qw, pool, nxt
         del wd, bias
         torch.cuda.empty_cache()
     fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
@@ -335,6 +383,73 @@ def bench_prefill(torch, w4, synth, reps: int):
         "min_tflops_m_ge_512": min(p["tflops"] for p in big),
         "points": pts,
     }
+
+
+def bench_single(torch, w4, synth):
+    """The single W4A16 matmul (X bf16 [4][2048], W fp32 [2048][2048] ~ N(0,0.02) quantized with
+    g=128, seed 0): GPU time per call with cold weights, and the host's enqueue cost per call
+    through the C ABI (the GPU parked on a spin meanwhile)."""
+    import numpy as np
+    x, w = synth.single_matmul_case()
+    qw = w4.quantize_pack(torch.from_numpy(w).cuda(), "groupwise", 128)
+    xd = dev_bf16(torch, x)
+    y = torch.empty((4, 2048), dtype=torch.float32, device="cuda")
+    nxt = rotating(weight_pool(w4, qw))
+    n = 200
+    t = timed(torch, [lambda: w4.mm(xd, nxt(), out=y)] * n) / n
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * 0.05))
+    h0 = time.perf_counter()
+    for _ in range(n):
+        w4.mm(xd, nxt(), out=y)
+    host_us = (time.perf_counter() - h0) * 1e6 / n
+    torch.cuda.synchronize()
+    b = gemv_bytes(4, 2048, 2048, 128)
+    return {"workload": "single W4A16 matmul: X bf16 [4][2048], W fp32 [2048][2048] g=128, seed 0",
+            "kernel": w4.kernel_for(4, 2048, 2048, "groupwise", 128), "us": round(t * 1e3, 3),
+            "GBps": round(b / (t * 1e-3) / 1e9, 1), "host_enqueue_us_per_call": round(host_us, 2)}
+
+
+MIDM_M = [8, 16, 32, 64, 100]
+
+
+def bench_midm(torch, w4, synth, reps: int):
+    """Mid-M (5 <= M < 128) at the decode layer shapes, g=128, both directions: TFLOP/s per point
+    with cold weights."""
+    log(f"mid-M GEMM: M in {MIDM_M} x {len(DECODE_SHAPES)} decode shapes x {{NT, T}}")
+    pts = []
+    for si, (N, K) in enumerate(DECODE_SHAPES):
+        qw = w4.quantize_pack(dev_bf16(torch, synth.weight(2, si, N, K, "bf16")), "groupwise", DECODE_G)
+        pool = weight_pool(w4, qw)
+        nxt = rotating(pool)
+        for M in MIDM_M:
+            x = dev_bf16(torch, synth.activations_bf16(6, si * 10 + M, M, K))
+            dy = dev_bf16(torch, synth.activations_bf16(6, si * 10 + M, M, N, tensor_id=synth.T_DY))
+            y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            dx = torch.empty((M, K), dtype=torch.float32, device="cuda")
+            t_nt = timed(torch, [lambda: w4.mm(x, nxt(), out=y)] * reps) / reps * 1e-3
+            t_t = timed(torch, [lambda: w4.mm(dy, nxt(), transposed=True, out=dx)] * reps) / reps * 1e-3
+            fl = 2.0 * M * N * K
+            b = N * K // 2 + 4 * N * (K // DECODE_G)
+            pts.append({"M": M, "N": N, "K": K, "nt_us": round(t_nt * 1e6, 2), "t_us": round(t_t * 1e6, 2),
+                        "nt_tflops": round(fl / t_nt / 1e12, 1), "t_tflops": round(fl / t_t / 1e12, 1),
+                        "nt_weight_GBps": round(b / t_nt / 1e9, 1),
+                        "nt_kernel": w4.kernel_for(M, N, K, "groupwise", DECODE_G),
+                        "t_kernel": w4.kernel_for(M, N, K, "groupwise", DECODE_G, True)})
+            del x, dy, y, dx
+        del qw, pool, nxt
+        torch.cuda.empty_cache()
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
+    by_m = {}
+    for M in MIDM_M:
+        sel = [p for p in pts if p["M"] == M]
+        f = sum(2.0 * p["M"] * p["N"] * p["K"] for p in sel)
+        by_m[str(M)] = {"nt_tflops": round(f / (sum(p["nt_us"] for p in sel) * 1e-6) / 1e12, 1),
+                        "t_tflops": round(f / (sum(p["t_us"] for p in sel) * 1e-6) / 1e12, 1)}
+    return {"workload": "mid-M GEMM at the decode layer shapes, g=128, M in {8, 16, 32, 64, 100}",
+            "nt_tflops": round(fl / (sum(p["nt_us"] for p in pts) * 1e-6) / 1e12, 1),
+            "t_tflops": round(fl / (sum(p["t_us"] for p in pts) * 1e-6) / 1e12, 1),
+            "by_M": by_m, "points": pts}
 
 
 def bench_quantize(torch, w4, synth, reps: int):
@@ -364,15 +479,27 @@ def bench_quantize(torch, w4, synth, reps: int):
     return {"workload": "fp16 W [128256][2048] ~ N(0,0.02) + 0.1% N(0,0.5) outliers", "points": out}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, budget_s: float):
-    """The CPU oracle on a bounded sample of the GEMV sweep (algorithmic GB/s)."""
+    """The CPU oracle on bounded samples: the matmul on the GEMV sweep (algorithmic GB/s, the
+    headline's unit) and, separately, the quantizer on rows of the quantize workload."""
     import numpy as np
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
+        blas_threads = os.cpu_count() or 1
     # shapes of the sweep in order, every M; stops once the budget of oracle time is spent
     sample = [(si, M) for si in (1, 0, 3, 2, 5) for M in (1, 2, 3, 4)]
     done, total_bytes, t_total = [], 0, 0.0
@@ -394,9 +521,24 @@ def cpu_baseline(synth, budget_s: float):
         done.append(f"{N}x{K}/M{M}")
         if t_total > budget_s:
             break
-    return {"value": round(total_bytes / t_total / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    # the quantizer (numpy elementwise, one thread) on the first 8192 rows of the quantize
+    # workload, g=128 and rowwise; GB/s counts the bytes the GPU kernel moves for those rows
+    wq = synth.weight_with_outliers(5, 0, 128256, 2048)[:8192]
+    w32 = O.to_f32(wq, "f16")
+    qt, qb = 0.0, 0
+    for mode, g in ((O.GROUPWISE, 128), (O.ROWWISE, None)):
+        t0 = time.perf_counter()
+        O.quantize_pack(w32, mode, g)
+        qt += time.perf_counter() - t0
+        pairs = w32.shape[0] * (w32.shape[1] // g if g else 1)
+        qb += w32.size * 2 + w32.size // 2 + 4 * pairs
+    return {"value": round(total_bytes / t_total / 1e9, 3), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
             "sample": "oracle matmul (bf16 dequantize + float64 BLAS product) on " + ", ".join(done) +
-                      f" of the decode sweep, {t_total:.1f} s"}
+                      f" of the decode sweep, {t_total:.1f} s",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "quantize": {"GBps": round(qb / qt / 1e9, 3), "cores": 1, "seconds": round(qt, 2),
+                         "sample": "oracle quantize_pack (numpy fp32, one thread) of fp16 [8192][2048] rows of "
+                                   "the quantize workload, g=128 and rowwise"}}
 
 
 def load_traffic(step_bytes_per_launch: float):
@@ -492,7 +634,16 @@ def main() -> int:
                      "per_shape_batches_gbs": None if args.sweep_only else round(g["per_point_gbs"], 1),
                      "sweep_after_idle_gbs": None if args.sweep_only else round(g["after_idle_gbs"], 1)},
     }
+    # every untimed lead-in ahead of a timed region, stated: the sweep honours --warmup alone
+    result["timing"] = {"sweep_lead_in_steps": args.warmup, "sweep_timed_steps": args.steps,
+                        "other_blocks_lead_in_ms": WARM_MS,
+                        "weights": "rotating through >= 1 GiB of copies wherever one copy fits the 256 MB "
+                                   "last-level cache (the quantize input, 525 MB, never fits)"}
     details = {"gemv": g["points"]}
+    if not args.sweep_only:
+        sm = bench_single(torch, w4, synth)
+        result["single_matmul"] = sm
+        log(f"single matmul: {sm['us']} us per call ({sm['kernel']}), host enqueue {sm['host_enqueue_us_per_call']} us")
     if not args.no_extras:
         gm = bench_gemm(torch, w4, synth, reps=10)
         result["gemm"] = {k: v for k, v in gm.items() if k not in ("points", "layer_points")}
@@ -507,6 +658,10 @@ def main() -> int:
         details["prefill"] = pf["points"]
         log(f"prefill GEMM: {pf['tflops']} TFLOP/s over the 45 points, by M {pf['tflops_by_M']}, "
             f"M >= 512 minimum {pf['min_tflops_m_ge_512']}")
+        mm_ = bench_midm(torch, w4, synth, reps=10)
+        result["midm"] = {k: v for k, v in mm_.items() if k != "points"}
+        details["midm"] = mm_["points"]
+        log(f"mid-M GEMM: NT {mm_['nt_tflops']} TFLOP/s, T {mm_['t_tflops']} TFLOP/s")
         qz = bench_quantize(torch, w4, synth, reps=10)
         result["quantize"] = {"workload": qz["workload"],
                               "GBps": {p["mode"]: p["GBps"] for p in qz["points"]},
@@ -517,7 +672,8 @@ def main() -> int:
     if not args.no_cpu:
         cb = cpu_baseline(synth, args.cpu_budget)
         result["cpu_baseline"] = cb
-        log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads")
+        log(f"cpu baseline: {cb['value']} GB/s on {cb['cores']} threads ({cb['cpu_model']}); quantize "
+            f"{cb['quantize']['GBps']} GB/s on 1 thread")
     else:
         result["cpu_baseline"] = None
     if args.details:
