@@ -627,8 +627,8 @@ namespace {
 
 // Tile configurations.  kind 0: the LDS-staged kernel above (both directions; the
 // non-transposed form only serves contractions too long for the register-operand kernel);
-// kind 1 / 2: the non-transposed register-operand kernel (gemm_nt.hip) with 128 x 128 /
-// 256 x 128 tiles.  slots: workgroups resident per CU; full: workgroups per CU needed for
+// kind 1-6: the non-transposed register-operand kernel (gemm_nt.hip): 128 x 128, 256 x 128,
+// 64 x 128, 32 x 128 with four waves, 256 x 256 and 128 x 256 with eight.  slots: workgroups resident per CU; full: workgroups per CU needed for
 // full throughput; eff: throughput of a full tile relative to the best of its direction,
 // all measured on MI355X at the fine-tune shapes.
 struct Cfg {
@@ -651,6 +651,9 @@ constexpr Cfg kCfgs[] = {
     {3, 1, 4, 2, 1, 64, 2, "gemm_nt_64x128", false, 4, 2, 0.85f},
     {4, 1, 4, 1, 1, 64, 2, "gemm_nt_32x128", false, 4, 2, 0.5f},
     {0, 1, 4, 1, 1, 64, 4, "gemm_t_32x128", true, 3, 2, 0.3f},
+    // eight waves side by side (256 columns) on one activation tile
+    {5, 1, 8, 8, 1, 64, 2, "gemm_nt_256x256", false, 1, 1, 1.02f},
+    {6, 1, 8, 4, 1, 64, 2, "gemm_nt_128x256", false, 2, 2, 0.94f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
@@ -737,6 +740,9 @@ Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
     const float edge = (float)a.M / (float)(tm * bm) * (float)outc / (float)(tn * bn);
     for (int sp = 1; sp <= (allow_split ? 8 : 1); sp *= 2) {
       if (sp > 1 && kt / sp < 16) break;  // keep >= 16 contraction steps per slice
+      // a one-workgroup-per-CU tile splits only when, unsplit, it would leave more than half
+      // the CUs idle (measured: split at half the CUs it lost 2-4% to an unsplit 128 x 128)
+      if (sp > 1 && c.slots == 1 && !a.transposed && 2 * tm * tn >= cus) break;
       const int64_t wgs = tm * tn * sp;
       const int64_t resident = cus * c.slots;
       float util;
@@ -754,7 +760,8 @@ Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
         best = Plan{i, sp};
       }
       // split tail: whole tile columns that fill the full rounds run unsplit, the rest split
-      if (sp == 1 && allow_split && wgs > resident && wgs % resident != 0) {
+      // (not for the forward one-workgroup-per-CU tile: measured slower than 128 x 128 unsplit)
+      if (sp == 1 && allow_split && (a.transposed || c.slots > 1) && wgs > resident && wgs % resident != 0) {
         const int64_t main_cols = wgs / resident * resident / tm;
         const int64_t tail_cols = tn - main_cols;
         if (main_cols > 0 && tail_cols > 0) {
@@ -866,6 +873,8 @@ hipError_t run_cfg(const MmArgs& a, int cfg, const GemmPart& gp, float* part, hi
     case 2: return launch_gemm_nt_reg(a, 1, gp, part, st);
     case 3: return launch_gemm_nt_reg(a, 2, gp, part, st);
     case 4: return launch_gemm_nt_reg(a, 3, gp, part, st);
+    case 5: return launch_gemm_nt_reg(a, 4, gp, part, st);
+    case 6: return launch_gemm_nt_reg(a, 5, gp, part, st);
     default: return run_meta<false, 2, 2, 4, 4, 64, 2>(a, gp, part, st);
   }
 }

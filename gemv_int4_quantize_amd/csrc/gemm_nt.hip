@@ -10,8 +10,10 @@
 // a weight row.  So each lane loads its own words (one dwordx4 = 32 contraction values of
 // one row per 64-wide step) and dequantizes them into operand registers; the weights never
 // pass through LDS.  Only the activation tile is staged in LDS (shared by the 4 waves).
-//   * workgroup = 4 waves side by side along N; wave w owns output columns
-//     [c0 + 32 FN w, +32 FN) and all BM = 32 FM rows of the tile;
+//   * workgroup = NW (4 or 8) waves side by side along N; wave w owns output columns
+//     [c0 + 32 FN w, +32 FN) and all BM = 32 FM rows of the tile.  Eight waves share one
+//     activation tile across 256 columns: half the activation loads (and L2 reads) per
+//     MFMA of four;
 //   * within a 64-wide contraction step the contraction order is permuted: MFMA step kk,
 //     operand slot 8 h + t (h = lane / 32) is contraction index k0 + 32 h + 8 kk + t, so a
 //     lane's four words for the step are contiguous; the activation fragment is read from
@@ -61,8 +63,8 @@ constexpr int kLR = 72;   // LDS row: 64 bf16 + 8 padding
 // one load form; SPL (META 1): the contraction steps one wide load covers (2, or 4 / 8 when
 // K allows: four or eight times fewer scale / zero loads).  One load holds the pairs of
 // SPL * 64 / g consecutive groups, so g = 128 SPL / WB when a group is at most 64 SPL wide.
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL>
-__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restrict__ A,
+template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_kernel(const uint16_t* __restrict__ A,
                                                          const int32_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros,
@@ -70,8 +72,10 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
                                                          int M, int N, int K, int meta_row, int log2g,
                                                          int kt_per_slice, int ct0, int pw,
                                                          float* __restrict__ part) {
-  constexpr int BM = FM * 32, BN = 4 * FN * 32;
-  constexpr int AU = BM * 8 / 256;  // 16-byte activation units per thread per step
+  constexpr int BM = FM * 32, BN = NW * FN * 32;
+  constexpr int NT = NW * 64;       // threads
+  constexpr int AU = BM * 8 / NT;   // 16-byte activation units per thread per step
+  static_assert(AU * NT == BM * 8, "whole activation units per thread");
   static_assert(!(DMA && KTAIL), "direct LDS loads cannot zero the columns past K");
   static_assert(SPL == 2 || (DMA && META == 1), "wide scale / zero loads over more than two steps: direct path");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   uint32_t a_off[AU];
 #pragma unroll
   for (int i = 0; i < AU; ++i) {
-    const int u = tid + i * 256;
+    const int u = tid + i * NT;
     const int ch = DMA ? ((u & 7) ^ ((u >> 5) & 7)) : (u & 7);
     a_off[i] = (uint32_t)((u >> 3) * K * 2 + ch * 16);
   }
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   auto store_a = [&](int kt, const ARegs& R, uint16_t* buf) {
 #pragma unroll
     for (int i = 0; i < AU; ++i) {
-      const int u = tid + i * 256;
+      const int u = tid + i * NT;
       u32x4 v = R.a[i];
       // past K the weight words are another row's (finite) codes: the activations must be 0
       if constexpr (KTAIL) {
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
         // the whole offset in the range-checked vector offset: reads past the tile's rows
         // (steps past the slice, rows past M) return zeros.  The explicit int matters: with
         // an unsigned argument the host pass silently drops the kernel's launch stub.
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(lds + buf * BUFB + (i * 256 + wave * 64) * 16), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(lds + buf * BUFB + (i * NT + wave * 64) * 16), 16,
                                                  (int)(a_off[i] + kt * kBK * 2), 0, 0, 0);
     };
     // Barrier once every load of this wave has landed (s_waitcnt vmcnt(0) lgkmcnt(0)).  The compiler
@@ -449,10 +453,10 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_kernel(const uint16_t* __restr
   }
 }
 
-template <int FM, int FN, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL = 2>
+template <int FM, int FN, int NW, int GPW, int META, bool KTAIL, int WB, bool F16, bool DMA, int SPL = 2>
 hipError_t launch_cfg(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
-  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA, SPL>;
-  constexpr int BM = FM * 32, BN = 4 * FN * 32;
+  auto k = gemm_nt_kernel<FM, FN, GPW, META, KTAIL, WB, F16, DMA, SPL, NW>;
+  constexpr int BM = FM * 32, BN = NW * FN * 32;
   const int lds = DMA ? 2 * BM * 128 : 2 * BM * kLR * 2;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -470,51 +474,51 @@ hipError_t launch_cfg(const MmArgs& a, const GemmPart& gp, float* part, hipStrea
   const int64_t c_lo = (int64_t)gp.ct0 * BN;
   const int pw = (int)(std::min<int64_t>(a.N, c_lo + (int64_t)nct * BN) - c_lo);
   const dim3 grid((unsigned)nct, (unsigned)((a.M + BM - 1) / BM), (unsigned)splits);
-  k<<<grid, 256, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K, meta_row,
+  k<<<grid, NW * 64, lds, st>>>(a.A, a.packed, a.scales, a.zeros, a.ep, (int)a.M, (int)a.N, (int)a.K, meta_row,
                             log2g, kts, gp.ct0, pw, splits > 1 ? part : nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, a.M, c_lo, pw, a.ep, st);
 }
 
-template <int FM, int FN, bool KTAIL, bool F16, bool DMA>
+template <int FM, int FN, int NW, bool KTAIL, bool F16, bool DMA>
 hipError_t launch_meta(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
-  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, 1, 0, KTAIL, 0, F16, DMA>(a, gp, part, st);
+  if (a.mode != W4_MODE_GROUPWISE) return launch_cfg<FM, FN, NW, 1, 0, KTAIL, 0, F16, DMA>(a, gp, part, st);
   const bool g16 = a.group == 16;
   if (a.K % 128 == 0) {
     // direct path: one 16- or 8-byte load covering 4 or 8 steps where K allows
     switch (a.group) {
-      case 16: return launch_cfg<FM, FN, 2, 1, KTAIL, 16, F16, DMA>(a, gp, part, st);
+      case 16: return launch_cfg<FM, FN, NW, 2, 1, KTAIL, 16, F16, DMA>(a, gp, part, st);
       case 32:
         if constexpr (DMA)
-          if (a.K % 256 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 16, F16, DMA, 4>(a, gp, part, st);
-        return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA>(a, gp, part, st);
+          if (a.K % 256 == 0) return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 16, F16, DMA, 4>(a, gp, part, st);
+        return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 8, F16, DMA>(a, gp, part, st);
       case 64:
         if constexpr (DMA) {
-          if (a.K % 512 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 16, F16, DMA, 8>(a, gp, part, st);
-          if (a.K % 256 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA, 4>(a, gp, part, st);
+          if (a.K % 512 == 0) return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 16, F16, DMA, 8>(a, gp, part, st);
+          if (a.K % 256 == 0) return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 8, F16, DMA, 4>(a, gp, part, st);
         }
-        return launch_cfg<FM, FN, 1, 1, KTAIL, 4, F16, DMA>(a, gp, part, st);
+        return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 4, F16, DMA>(a, gp, part, st);
       case 128:
         if constexpr (DMA)
-          if (a.K % 512 == 0) return launch_cfg<FM, FN, 1, 1, KTAIL, 8, F16, DMA, 8>(a, gp, part, st);
-        return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
-      default: return launch_cfg<FM, FN, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
+          if (a.K % 512 == 0) return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 8, F16, DMA, 8>(a, gp, part, st);
+        return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
+      default: return launch_cfg<FM, FN, NW, 1, 1, KTAIL, 2, F16, DMA>(a, gp, part, st);
     }
   }
-  return g16 ? launch_cfg<FM, FN, 2, 2, KTAIL, 0, F16, DMA>(a, gp, part, st)
-             : launch_cfg<FM, FN, 1, 2, KTAIL, 0, F16, DMA>(a, gp, part, st);
+  return g16 ? launch_cfg<FM, FN, NW, 2, 2, KTAIL, 0, F16, DMA>(a, gp, part, st)
+             : launch_cfg<FM, FN, NW, 1, 2, KTAIL, 0, F16, DMA>(a, gp, part, st);
 }
 
-template <int FM, int FN>
+template <int FM, int FN, int NW>
 hipError_t launch_tile(const MmArgs& a, const GemmPart& gp, float* part, hipStream_t st) {
   // K % 64 == 0: direct LDS loads of the activation tile; otherwise the register path,
   // which zeroes the activation columns past K
   if (a.K % kBK != 0)
-    return a.a_f16 ? launch_meta<FM, FN, true, true, false>(a, gp, part, st)
-                   : launch_meta<FM, FN, true, false, false>(a, gp, part, st);
-  return a.a_f16 ? launch_meta<FM, FN, false, true, true>(a, gp, part, st)
-                 : launch_meta<FM, FN, false, false, true>(a, gp, part, st);
+    return a.a_f16 ? launch_meta<FM, FN, NW, true, true, false>(a, gp, part, st)
+                   : launch_meta<FM, FN, NW, true, false, false>(a, gp, part, st);
+  return a.a_f16 ? launch_meta<FM, FN, NW, false, true, true>(a, gp, part, st)
+                 : launch_meta<FM, FN, NW, false, false, true>(a, gp, part, st);
 }
 
 }  // namespace
@@ -526,10 +530,12 @@ bool gemm_nt_reg_supported(const MmArgs& a) {
 
 hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, const GemmPart& gp, float* part, hipStream_t st) {
   switch (tile) {
-    case 0: return launch_tile<4, 1>(a, gp, part, st);  // 128 x 128
-    case 1: return launch_tile<8, 1>(a, gp, part, st);  // 256 x 128
-    case 2: return launch_tile<2, 1>(a, gp, part, st);  // 64 x 128
-    default: return launch_tile<1, 1>(a, gp, part, st);  // 32 x 128
+    case 0: return launch_tile<4, 1, 4>(a, gp, part, st);  // 128 x 128
+    case 1: return launch_tile<8, 1, 4>(a, gp, part, st);  // 256 x 128
+    case 2: return launch_tile<2, 1, 4>(a, gp, part, st);  // 64 x 128
+    case 4: return launch_tile<8, 1, 8>(a, gp, part, st);  // 256 x 256, eight waves
+    case 5: return launch_tile<4, 1, 8>(a, gp, part, st);  // 128 x 256, eight waves
+    default: return launch_tile<1, 1, 4>(a, gp, part, st);  // 32 x 128
   }
 }
 

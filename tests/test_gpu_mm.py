@@ -261,6 +261,54 @@ def test_split_tail_gemm(ci):
             assert_mm_close(got, want, f"{what} {ci}")
 
 
+EIGHT_WAVE_CASES = [  # (M, N, K, mode, g, fp16 activations, bf16 output with bias, expected kernel)
+    (1500, 8200, 256, "groupwise", 16, False, False, "gemm_nt_256x256"),
+    (1500, 8200, 2080, "groupwise", 32, False, True, "gemm_nt_256x256"),
+    (300, 20000, 256, "groupwise", 64, True, False, "gemm_nt_128x256"),
+    (300, 20000, 320, "global", None, False, True, "gemm_nt_128x256"),
+    (1024, 4096, 11008, "rowwise", None, False, False, "gemm_nt_256x256_splitk4"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(EIGHT_WAVE_CASES)),
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}{c[3]}{c[4] or ''}" for c in EIGHT_WAVE_CASES])
+def test_eight_wave_tiles(ci):
+    """The forward tiles with eight waves on one activation tile (256 output columns):
+    ragged M and N, two groups per lane chunk (g = 16), a contraction that is not a whole
+    number of 64-wide steps (register route), fp16 activations, bf16 output with bias, and
+    a split contraction.  Sampled rows (tile edges included) match the oracle; the results
+    are deterministic."""
+    M, N, K, mode, g, f16, epi, kern = EIGHT_WAVE_CASES[ci]
+    print(f"[case] eight-wave M={M} N={N} K={K} {mode}{g or ''} f16={f16} epi={epi}", flush=True)
+    assert w4.kernel_for(M, N, K, mode, g) == kern
+    w = synth.weight(712, ci, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
+    qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
+    a = synth.activations_bf16(712, ci, M, K)
+    if f16:
+        a = O.bf16_bits_to_f64(a).astype(np.float16).view(np.uint16)  # the bf16 draw, rounded to fp16
+        ad = torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.float16)
+    else:
+        ad = dev_bf16(a)
+    bias = O.bf16_bits_to_f64(O.bf16_rne_bits(synth.bias_f32(712, ci, N))) if epi else None
+    if epi:
+        kw = dict(bias=torch.from_numpy(bias.astype(np.float32)).to(DEV).to(torch.bfloat16), out_dtype=torch.bfloat16)
+    else:
+        kw = {}
+    y1 = w4.mm(ad, qw, **kw)
+    assert torch.equal(y1, w4.mm(ad, qw, **kw))
+    ms = _edge_idx(M, np.random.default_rng(ci), 12)
+    got = host(y1[torch.from_numpy(ms).to(DEV)].float()).astype(np.float64)
+    want = O.matmul(a[ms], *ref, K, a_dtype="f16" if f16 else "bf16")
+    if epi:
+        want = O.round_output(want + bias, "bf16")
+        ulp = np.abs(want) * 2.0**-7
+        bad = np.abs(got - want) > ELEM_RTOL * np.abs(want) + ELEM_ATOL + ulp
+        assert not bad.any(), f"{int(bad.sum())} elements outside the bound, case {ci}"
+    else:
+        assert_mm_close(got, want, f"eight-wave {ci}")
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled outputs
 
 DECODE_SHAPES = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (2048, 2048), (8192, 8192),
