@@ -640,7 +640,7 @@ struct Cfg {
   float eff;
 };
 constexpr Cfg kCfgs[] = {
-    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 1.06f},
+    {0, 2, 2, 4, 4, 64, 4, "gemm_t_256x256", true, 1, 1, 0.98f},
     {0, 4, 2, 2, 2, 64, 4, "gemm_t_256x128", true, 1, 1, 1.0f},
     {0, 2, 2, 2, 2, 32, 4, "gemm_t_128x128", true, 3, 2, 0.65f},
     {1, 1, 4, 4, 1, 64, 2, "gemm_nt_128x128", false, 3, 2, 0.92f},
@@ -654,6 +654,9 @@ constexpr Cfg kCfgs[] = {
     // eight waves side by side (256 columns) on one activation tile
     {5, 1, 8, 8, 1, 64, 2, "gemm_nt_256x256", false, 1, 1, 1.02f},
     {6, 1, 8, 4, 1, 64, 2, "gemm_nt_128x256", false, 2, 2, 0.94f},
+    // transposed 256 x 256 with eight waves (2 x 4, each 128 x 64): two waves per SIMD where
+    // the four-wave form has one, and the same LDS tiles
+    {0, 2, 4, 4, 2, 64, 4, "gemm_t_w8_256x256", true, 1, 1, 1.25f},
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 constexpr int kNtLdsCfg = 5;
@@ -865,6 +868,7 @@ hipError_t run_cfg(const MmArgs& a, int cfg, const GemmPart& gp, float* part, hi
       case 0: return run_meta<true, 2, 2, 4, 4, 64, 4>(a, gp, part, st);
       case 1: return run_meta<true, 4, 2, 2, 2, 64, 4>(a, gp, part, st);
       case 8: return run_meta<true, 1, 4, 1, 1, 64, 4>(a, gp, part, st);
+      case 11: return run_meta<true, 2, 4, 4, 2, 64, 4>(a, gp, part, st);
       default: return run_meta<true, 2, 2, 2, 2, 32, 4>(a, gp, part, st);
     }
   }

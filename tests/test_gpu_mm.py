@@ -210,8 +210,8 @@ def test_splitk_gemm(ci):
     assert_mm_close(host(y0), want, f"unsplit {ci}")
 
 
-TAIL_CASES = [(1536, 2048, 6144, True, "rowwise", None, False), (1536, 11008, 2048, False, "rowwise", None, True),
-              (1024, 2048, 11008, True, "groupwise", 64, True), (1536, 11008, 2048, False, "groupwise", 128, False)]
+TAIL_CASES = [(1536, 2048, 11008, True, "rowwise", None, False), (1536, 11008, 2048, False, "rowwise", None, True),
+              (768, 2048, 11008, True, "groupwise", 64, True), (1536, 11008, 2048, False, "groupwise", 128, False)]
 
 
 @pytest.mark.parametrize("ci", range(len(TAIL_CASES)),
@@ -261,45 +261,50 @@ def test_split_tail_gemm(ci):
             assert_mm_close(got, want, f"{what} {ci}")
 
 
-EIGHT_WAVE_CASES = [  # (M, N, K, mode, g, fp16 activations, bf16 output with bias, expected kernel)
-    (1500, 8200, 256, "groupwise", 16, False, False, "gemm_nt_256x256"),
-    (1500, 8200, 2080, "groupwise", 32, False, True, "gemm_nt_256x256"),
-    (300, 20000, 256, "groupwise", 64, True, False, "gemm_nt_128x256"),
-    (300, 20000, 320, "global", None, False, True, "gemm_nt_128x256"),
-    (1024, 4096, 11008, "rowwise", None, False, False, "gemm_nt_256x256_splitk4"),
+EIGHT_WAVE_CASES = [  # (M, N, K, transposed, mode, g, fp16 activations, bf16 output with bias, expected kernel)
+    (1500, 8200, 256, False, "groupwise", 16, False, False, "gemm_nt_256x256"),
+    (1500, 8200, 2080, False, "groupwise", 32, False, True, "gemm_nt_256x256"),
+    (300, 20000, 256, False, "groupwise", 64, True, False, "gemm_nt_128x256"),
+    (300, 20000, 320, False, "global", None, False, True, "gemm_nt_128x256"),
+    (1024, 4096, 11008, False, "rowwise", None, False, False, "gemm_nt_256x256_splitk4"),
+    (700, 1024, 12320, True, "groupwise", 16, False, False, "gemm_t_w8_256x256"),
+    (500, 8200, 2080, True, "groupwise", 32, True, True, "gemm_t_w8_256x256_splitk8"),
+    (1000, 4104, 2080, True, "global", None, False, True, "gemm_t_w8_256x256_splitk4"),
 ]
 
 
 @pytest.mark.parametrize("ci", range(len(EIGHT_WAVE_CASES)),
-                         ids=[f"{c[0]}x{c[1]}x{c[2]}{c[3]}{c[4] or ''}" for c in EIGHT_WAVE_CASES])
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}{'t' if c[3] else 'nt'}{c[4]}{c[5] or ''}" for c in EIGHT_WAVE_CASES])
 def test_eight_wave_tiles(ci):
-    """The forward tiles with eight waves on one activation tile (256 output columns):
-    ragged M and N, two groups per lane chunk (g = 16), a contraction that is not a whole
-    number of 64-wide steps (register route), fp16 activations, bf16 output with bias, and
-    a split contraction.  Sampled rows (tile edges included) match the oracle; the results
-    are deterministic."""
-    M, N, K, mode, g, f16, epi, kern = EIGHT_WAVE_CASES[ci]
-    print(f"[case] eight-wave M={M} N={N} K={K} {mode}{g or ''} f16={f16} epi={epi}", flush=True)
-    assert w4.kernel_for(M, N, K, mode, g) == kern
+    """The tiles with eight waves on one workgroup's LDS tiles: forward 256 x 256 and
+    128 x 256 (one activation tile across 256 output columns) and transposed 256 x 256 (2 x 4
+    waves of 128 x 64).  Ragged M and output columns, a partial last contraction step, two
+    groups per lane chunk (g = 16), a contraction that is not a whole number of 64-wide
+    steps on the forward register route, fp16 activations, bf16 output with bias, split
+    contractions.  Sampled rows (tile edges included) match the oracle; the results are
+    deterministic."""
+    M, N, K, t, mode, g, f16, epi, kern = EIGHT_WAVE_CASES[ci]
+    print(f"[case] eight-wave M={M} N={N} K={K} t={t} {mode}{g or ''} f16={f16} epi={epi}", flush=True)
+    assert w4.kernel_for(M, N, K, mode, g, transposed=t) == kern
     w = synth.weight(712, ci, N, K, "bf16")
     ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
     qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)
-    a = synth.activations_bf16(712, ci, M, K)
+    outc = K if t else N
+    a = synth.activations_bf16(712, ci, M, N if t else K)
     if f16:
         a = O.bf16_bits_to_f64(a).astype(np.float16).view(np.uint16)  # the bf16 draw, rounded to fp16
         ad = torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.float16)
     else:
         ad = dev_bf16(a)
-    bias = O.bf16_bits_to_f64(O.bf16_rne_bits(synth.bias_f32(712, ci, N))) if epi else None
+    bias = O.bf16_bits_to_f64(O.bf16_rne_bits(synth.bias_f32(712, ci, outc))) if epi else None
+    kw = dict(transposed=t)
     if epi:
-        kw = dict(bias=torch.from_numpy(bias.astype(np.float32)).to(DEV).to(torch.bfloat16), out_dtype=torch.bfloat16)
-    else:
-        kw = {}
+        kw.update(bias=torch.from_numpy(bias.astype(np.float32)).to(DEV).to(torch.bfloat16), out_dtype=torch.bfloat16)
     y1 = w4.mm(ad, qw, **kw)
     assert torch.equal(y1, w4.mm(ad, qw, **kw))
     ms = _edge_idx(M, np.random.default_rng(ci), 12)
     got = host(y1[torch.from_numpy(ms).to(DEV)].float()).astype(np.float64)
-    want = O.matmul(a[ms], *ref, K, a_dtype="f16" if f16 else "bf16")
+    want = O.matmul(a[ms], *ref, K, transposed=t, a_dtype="f16" if f16 else "bf16")
     if epi:
         want = O.round_output(want + bias, "bf16")
         ulp = np.abs(want) * 2.0**-7
