@@ -609,15 +609,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 }
 
 // Split-K reduction: output columns [c_lo, c_lo + pw) = epilogue(sum over the S partial
-// [M][pw] planes, in a fixed order).
+// [M][pw] planes, in a fixed order).  VEC (pw and c_lo multiples of 4): four consecutive
+// columns per thread, one 16-byte load per plane, and one 16-byte store for a plain fp32
+// output with 16-byte aligned rows; the same sums, bit for bit.
+template <bool VEC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
                                                             int64_t c_lo, int64_t pw, const Epi ep) {
   const int64_t total = M * pw;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    float v = part[i];
-    for (int s = 1; s < S; ++s) v += part[(size_t)s * total + i];
-    const int64_t m = i / pw, c = i - m * pw;
-    epi_put(ep, epi_col(ep, c_lo + c), m, v);
+  if constexpr (!VEC) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+      float v = part[i];
+      for (int s = 1; s < S; ++s) v += part[(size_t)s * total + i];
+      const int64_t m = i / pw, c = i - m * pw;
+      epi_put(ep, epi_col(ep, c_lo + c), m, v);
+    }
+  } else {
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const bool wide = ep.dt == W4_DT_F32 && ep.nseg == 1 && (ep.ld[0] & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(ep.y[0]) & 15) == 0;
+    const f32x4v* p4 = reinterpret_cast<const f32x4v*>(part);
+    const int64_t total4 = total >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (int64_t)gridDim.x * 256) {
+      f32x4v v = __builtin_nontemporal_load(p4 + i);
+      for (int s = 1; s < S; ++s) v += __builtin_nontemporal_load(p4 + (size_t)s * total4 + i);
+      const int64_t m = (i << 2) / pw, c = (i << 2) - m * pw;
+      if (wide) {
+        const float* bias = static_cast<const float*>(ep.bias);
+        f32x4v o = v;
+        if (bias != nullptr) o += f32x4v{bias[c_lo + c], bias[c_lo + c + 1], bias[c_lo + c + 2], bias[c_lo + c + 3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4v*>(static_cast<float*>(ep.y[0]) + m * ep.ld[0] + c_lo + c));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) epi_put(ep, epi_col(ep, c_lo + c + u), m, v[u]);
+      }
+    }
   }
 }
 
@@ -907,8 +932,13 @@ Plan launched_plan(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
 
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t c_lo, int64_t pw, const Epi& ep,
                                 hipStream_t st) {
-  const int64_t blocks = (M * pw + 255) / 256;
-  splitk_reduce_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, c_lo, pw, ep);
+  if (pw % 4 == 0 && c_lo % 4 == 0) {
+    const int64_t blocks = (M * pw / 4 + 255) / 256;
+    splitk_reduce_kernel<true><<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, c_lo, pw, ep);
+  } else {
+    const int64_t blocks = (M * pw + 255) / 256;
+    splitk_reduce_kernel<false><<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, st>>>(part, splits, M, c_lo, pw, ep);
+  }
   return hipGetLastError();
 }
 
