@@ -25,8 +25,16 @@ def mode_id(mode) -> int:
     return int(mode)
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current HIP stream of `device` (the raw handle; about 2 us cheaper per call than
+    building torch's stream object)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(idx))
+    return ctypes.c_void_p(torch.cuda.current_stream(idx).cuda_stream)
 
 
 def _ptr(t: torch.Tensor | None):
@@ -233,6 +241,8 @@ _ODT = {torch.float32: DT_F32, torch.float16: DT_F16, torch.bfloat16: DT_BF16}
 
 
 def _workspace(qw: QuantizedWeight, M: int, transposed: bool, split_k: bool, device):
+    if not transposed and 0 <= M <= 4:
+        return None, 0  # the decode GEMV takes no workspace (w4_workspace_bytes reports 0)
     ws_bytes = ctypes.c_size_t(0)
     if split_k:
         op = _lib.OP_MM_T if transposed else _lib.OP_MM
@@ -290,8 +300,28 @@ def mm(a: torch.Tensor, qw: QuantizedWeight, transposed: bool = False, bias: tor
         out = torch.empty((max(M, 0), outc), dtype=dt, device=a.device)
     elif out.shape != (M, outc) or out.dtype != dt or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor of the output shape and dtype")
-    _mm_out(a, qw, transposed, bias, [out], split_k)
+    if (dt is torch.float32 and a.dtype is torch.bfloat16 and (bias is None or bias.dtype is torch.float32)
+            and M >= 0):
+        _mm_f32(a, qw, transposed, bias, out, split_k)  # the common case: w4a16_mm itself
+    else:
+        _mm_out(a, qw, transposed, bias, [out], split_k)
     return out
+
+
+def _mm_f32(a: torch.Tensor, qw: QuantizedWeight, transposed: bool, bias, out: torch.Tensor, split_k: bool):
+    """bf16 activations, fp32 output and bias: one w4a16_mm call (the checks of _mm_out)."""
+    _need_cuda(a, qw.packed, bias, out)
+    if not a.is_contiguous():
+        raise ValueError("activations must be a contiguous 2-D tensor")
+    M, L = a.shape
+    if L != (qw.N if transposed else qw.K):
+        raise ValueError(f"activation width {L} does not match the weight ({qw.N}x{qw.K}, transposed={transposed})")
+    outc = out.shape[1]
+    if bias is not None and (bias.numel() != outc or not bias.is_contiguous()):
+        raise ValueError(f"bias must be a contiguous torch.float32 vector of length {outc}")
+    ws, ws_bytes = _workspace(qw, M, transposed, split_k, a.device)
+    check(lib().w4a16_mm(_ptr(a), M, _ptr(qw.packed), _ptr(qw.scales), _ptr(qw.zeros), ctypes.byref(qw.desc()),
+                         1 if transposed else 0, _ptr(bias), _ptr(out), _ptr(ws), ws_bytes, _stream(a.device)))
 
 
 def mm_split(a: torch.Tensor, qw: QuantizedWeight, outs: list[torch.Tensor], bias: torch.Tensor | None = None,
