@@ -440,15 +440,24 @@ def bench_midm(torch, w4, synth, reps: int):
         del qw, pool, nxt
         torch.cuda.empty_cache()
     fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in pts)
+
+    def wbytes(p):  # algorithmic bytes: weights, scales and zeros, activations, fp32 output
+        return p["N"] * p["K"] // 2 + 4 * p["N"] * (p["K"] // DECODE_G) + 2 * p["M"] * p["K"] + 4 * p["M"] * p["N"]
+
     by_m = {}
     for M in MIDM_M:
         sel = [p for p in pts if p["M"] == M]
         f = sum(2.0 * p["M"] * p["N"] * p["K"] for p in sel)
-        by_m[str(M)] = {"nt_tflops": round(f / (sum(p["nt_us"] for p in sel) * 1e-6) / 1e12, 1),
-                        "t_tflops": round(f / (sum(p["t_us"] for p in sel) * 1e-6) / 1e12, 1)}
+        t_nt = sum(p["nt_us"] for p in sel) * 1e-6
+        by_m[str(M)] = {"nt_tflops": round(f / t_nt / 1e12, 1),
+                        "t_tflops": round(f / (sum(p["t_us"] for p in sel) * 1e-6) / 1e12, 1),
+                        "nt_GBps": round(sum(wbytes(p) for p in sel) / t_nt / 1e9, 1)}
+    sel = [p for p in pts if p["M"] <= 32]
+    nt_gbps = sum(wbytes(p) for p in sel) / (sum(p["nt_us"] for p in sel) * 1e-6) / 1e9
     return {"workload": "mid-M GEMM at the decode layer shapes, g=128, M in {8, 16, 32, 64, 100}",
             "nt_tflops": round(fl / (sum(p["nt_us"] for p in pts) * 1e-6) / 1e12, 1),
             "t_tflops": round(fl / (sum(p["t_us"] for p in pts) * 1e-6) / 1e12, 1),
+            "nt_m_le_32": {"GBps": round(nt_gbps, 1), "frac_of_hbm_peak": round(nt_gbps / HBM_PEAK_GBS, 4)},
             "by_M": by_m, "points": pts}
 
 
@@ -661,7 +670,8 @@ def main() -> int:
         mm_ = bench_midm(torch, w4, synth, reps=10)
         result["midm"] = {k: v for k, v in mm_.items() if k != "points"}
         details["midm"] = mm_["points"]
-        log(f"mid-M GEMM: NT {mm_['nt_tflops']} TFLOP/s, T {mm_['t_tflops']} TFLOP/s")
+        log(f"mid-M GEMM: NT {mm_['nt_tflops']} TFLOP/s, T {mm_['t_tflops']} TFLOP/s; "
+            f"NT at M <= 32 {mm_['nt_m_le_32']['GBps']} GB/s")
         qz = bench_quantize(torch, w4, synth, reps=10)
         result["quantize"] = {"workload": qz["workload"],
                               "GBps": {p["mode"]: p["GBps"] for p in qz["points"]},

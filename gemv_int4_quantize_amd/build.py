@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a16.so")
-SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemm.hip", "gemm_nt.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemv.hip", "gemm.hip", "gemm_nt.hip", "skinny.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -745,12 +745,15 @@ Plan pick_plan_small(const MmArgs& a, const DeviceCaps& caps, bool allow_split) 
   return best;
 }
 
+// W4A16_GEMM_CFG (an A/B benchmarking override) forces one tile configuration; set to any
+// value it also keeps mid-M problems on the tiles instead of the mid-M kernel.
+const char* gemm_cfg_env() {
+  static const char* e = getenv("W4A16_GEMM_CFG");
+  return e;
+}
+
 Plan pick_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split) {
-  static const int forced = [] {
-    // W4A16_GEMM_CFG forces one tile configuration (an A/B benchmarking override)
-    const char* e = getenv("W4A16_GEMM_CFG");
-    return e != nullptr ? atoi(e) : -1;
-  }();
+  static const int forced = gemm_cfg_env() != nullptr ? atoi(gemm_cfg_env()) : -1;
   const int64_t outc = a.transposed ? a.K : a.N;
   const int64_t L = a.transposed ? a.N : a.K;
   if (forced < 0 && !a.transposed && a.M >= 128 && 2.0 * a.M * outc * L < kSmallFlops)
@@ -924,6 +927,15 @@ hipError_t run_plan(const MmArgs& a, const Plan& p, float* part, hipStream_t st)
   return run_cfg(a, p.cfg, GemmPart{p.tail_splits, tn - p.tail_cols, p.tail_cols}, part, st);
 }
 
+// The mid-M kernel's plan for a launch with a workspace of ws_bytes (the split plan when its
+// planes fit, else the unsplit one); ok = false when the tiles run instead.
+SkinnyPlan launched_skinny(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  if (gemm_cfg_env() != nullptr || !skinny_supported(a)) return SkinnyPlan{};
+  SkinnyPlan p = skinny_plan(a, caps, ws_bytes > 0);
+  if (p.ok && skinny_split_bytes(a, p) > ws_bytes) p = skinny_plan(a, caps, false);
+  return p;
+}
+
 // The plan a launch with a workspace of ws_bytes runs: the split plan when it fits the
 // workspace, else the unsplit one.
 Plan launched_plan(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
@@ -948,6 +960,8 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_
 
 const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
   static thread_local char buf[64];
+  const SkinnyPlan sp = launched_skinny(a, caps, ws_bytes);
+  if (sp.ok) return skinny_name(a, sp);
   const Plan p = launched_plan(a, caps, ws_bytes);
   const Cfg& c = kCfgs[p.cfg];
   if (p.tail_cols > 0) {
@@ -960,18 +974,28 @@ const char* gemm_name(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) 
 }
 
 size_t gemm_lds_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  const SkinnyPlan sp = launched_skinny(a, caps, ws_bytes);
+  if (sp.ok) return sp.lds;
   return lds_bytes(kCfgs[launched_plan(a, caps, ws_bytes).cfg]);
 }
 
 size_t gemm_used_workspace_bytes(const MmArgs& a, const DeviceCaps& caps, size_t ws_bytes) {
+  const SkinnyPlan sp = launched_skinny(a, caps, ws_bytes);
+  if (sp.ok) return skinny_split_bytes(a, sp);
   return split_bytes(a, launched_plan(a, caps, ws_bytes));
 }
 
 size_t gemm_workspace_bytes(const MmArgs& a, const DeviceCaps& caps) {
+  if (gemm_cfg_env() == nullptr && skinny_supported(a)) {
+    const SkinnyPlan sp = skinny_plan(a, caps, true);
+    if (sp.ok) return skinny_split_bytes(a, sp);
+  }
   return split_bytes(a, pick_plan(a, caps, true));
 }
 
 hipError_t launch_gemm(const MmArgs& a, const DeviceCaps& caps, void* ws, size_t ws_bytes, hipStream_t st) {
+  const SkinnyPlan sp = launched_skinny(a, caps, ws != nullptr ? ws_bytes : 0);
+  if (sp.ok) return launch_skinny(a, sp, static_cast<float*>(ws), st);
   return run_plan(a, launched_plan(a, caps, ws != nullptr ? ws_bytes : 0), static_cast<float*>(ws), st);
 }
 

@@ -83,6 +83,26 @@ struct GemmPart {
 bool gemm_nt_reg_supported(const MmArgs& a);
 hipError_t launch_gemm_nt_reg(const MmArgs& a, int tile, const GemmPart& gp, float* part, hipStream_t st);
 
+// Mid-M forward matmul (kSkinnyMinM <= M <= kSkinnyMaxM) on 16x16x32 MFMAs with the
+// activations held in registers (skinny.hip).  A plan covers the rows in `blocks` blocks of
+// `rpb` rows and the contraction in `splits` ranges of `units_per_split` 128-column units;
+// with splits > 1 the sums go to [splits][M][N] fp32 planes and the split-K reduction
+// finishes them.  ok = false: this problem does not fit the kernel (the GEMM tiles run).
+constexpr int kSkinnyMinM = 5, kSkinnyMaxM = 32;
+struct SkinnyPlan {
+  bool ok = false;
+  int MB = 1, UP = 1;  // 16-row blocks of X; 128-column units per wave
+  int splits = 1, units_per_split = 0;
+  int rpb = 0, blocks = 0;
+  int log2gr = 0;  // the partial sums are reduced in rounds of 2^log2gr 16-row groups
+  size_t lds = 0;
+};
+bool skinny_supported(const MmArgs& a);
+SkinnyPlan skinny_plan(const MmArgs& a, const DeviceCaps& caps, bool allow_split);
+size_t skinny_split_bytes(const MmArgs& a, const SkinnyPlan& p);
+const char* skinny_name(const MmArgs& a, const SkinnyPlan& p);
+hipError_t launch_skinny(const MmArgs& a, const SkinnyPlan& p, float* part, hipStream_t st);
+
 // Output columns [c_lo, c_lo + pw) = epilogue(sum of `splits` fp32 [M][pw] planes, in a
 // fixed order).
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t c_lo, int64_t pw, const Epi& ep,

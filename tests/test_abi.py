@@ -84,6 +84,15 @@ def test_workspace_bytes():
         assert L.w4_workspace_bytes(ctypes.byref(d), op, 8192, ctypes.byref(b)) == 0 and b.value == 0
         assert "_splitk" not in w4.kernel_for(8192, 4096, 4096, "groupwise", 128, transposed=op == _lib.OP_MM_T)
     assert L.w4_workspace_bytes(ctypes.byref(d), 99, 4, ctypes.byref(b)) == _lib.W4_ERR_INVALID
+    # the mid-M kernel (5 <= M <= 32, forward) splits rows longer than one block covers
+    # (64 units of 128 columns at M <= 16, 32 at M <= 32) over planes [S][M][N]
+    d = _lib.W4Desc(4096, 16384, _lib.MODE_GROUPWISE, 128)
+    for M, S in ((16, 2), (32, 4)):
+        assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM, M, ctypes.byref(b)) == 0
+        assert w4.kernel_for(M, 4096, 16384, "groupwise", 128) == f"skinny_m{16 if M <= 16 else 32}_splitk{S}"
+        assert b.value == S * M * 4096 * 4
+    d = _lib.W4Desc(4096, 8192, _lib.MODE_GROUPWISE, 128)
+    assert L.w4_workspace_bytes(ctypes.byref(d), _lib.OP_MM, 8, ctypes.byref(b)) == 0 and b.value == 0
     # a partial last round: whole rounds of tile columns unsplit, the last columns split
     # into compact planes [S][M][columns past the unsplit ones]
     d = _lib.W4Desc(4096, 11008, _lib.MODE_ROWWISE, 0)
@@ -144,10 +153,13 @@ def test_quantize_validation_before_launch():
 
 
 def test_dispatch_names():
-    # decode shapes go to the GEMV, prefill / fine-tune shapes and the transposed mode to the MFMA GEMM
+    # decode shapes go to the GEMV, 5 <= M <= 32 forward to the mid-M kernel, prefill /
+    # fine-tune shapes and the transposed mode to the MFMA GEMM
     for M in (1, 2, 3, 4):
         assert w4.kernel_for(M, 4096, 4096, "groupwise", 128) == f"gemv_m{M}"
-    assert w4.kernel_for(5, 4096, 4096, "groupwise", 128).startswith("gemm_nt_")
+    assert w4.kernel_for(5, 4096, 4096, "groupwise", 128) == "skinny_m16"
+    assert w4.kernel_for(32, 4096, 4096, "groupwise", 128) == "skinny_m32"
+    assert w4.kernel_for(33, 4096, 4096, "groupwise", 128).startswith("gemm_nt_")
     assert w4.kernel_for(2048, 12288, 4096, "rowwise", None).startswith("gemm_nt_")
     assert w4.kernel_for(2048, 12288, 4096, "groupwise", 64, transposed=True).startswith("gemm_t_")
     assert w4.kernel_for(4, 4096, 4096, "groupwise", 128, transposed=True).startswith("gemm_t_")

@@ -47,6 +47,7 @@ def assert_rounded_close(y: np.ndarray, ref64: np.ndarray, dt: str, what: str):
 
 # (M, N, K, transposed, expected kernel prefix)
 CASES = [(1, 1000, 2048, False, "gemv_m1"), (3, 520, 4096, False, "gemv_m3"),
+         (16, 1000, 4096, False, "skinny_m16"), (24, 520, 8192, False, "skinny_m32_splitk"),
          (200, 1000, 2048, False, "gemm_nt"), (96, 4096, 8192, False, "gemm_nt"),
          (256, 1000, 2048, True, "gemm_t"), (64, 2048, 4096, True, "gemm_t")]
 
@@ -74,7 +75,7 @@ def test_output_dtype_and_bias(dt, ci, mode, g):
     assert torch.equal(y, y32.to(TDT[dt]))
 
 
-@pytest.mark.parametrize("M", [1, 4, 130, 512])
+@pytest.mark.parametrize("M", [1, 4, 16, 130, 512])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_fused_qkv_segments(M, dt):
     """One launch over a fused Q/K/V weight writes Q, K and V to separate tensors."""
@@ -100,7 +101,7 @@ def test_fused_qkv_segments(M, dt):
         assert torch.equal(o, whole[:, offs[i]:offs[i + 1]])
 
 
-@pytest.mark.parametrize("M,tr", [(2, False), (256, False), (128, True)])
+@pytest.mark.parametrize("M,tr", [(2, False), (24, False), (256, False), (128, True)])
 def test_segments_into_strided_views(M, tr):
     """Segments with row strides wider than their columns (views into a padded buffer):
     every output lands in place and the padding is left untouched."""

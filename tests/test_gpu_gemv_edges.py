@@ -72,11 +72,14 @@ def test_gemv_meta_any_alignment(mode, g, offs):
 @pytest.mark.parametrize("K", [(1 << 21) + 32, (1 << 21) + 64], ids=["ragged", "whole"])
 @pytest.mark.parametrize("mode,g", [("rowwise", None), ("groupwise", 32)], ids=["rowwise", "g32"])
 def test_nt_lds_tile_long_contraction(K, mode, g):
-    """M = 8 past K = 2^21 runs the non-transposed LDS tile; with K % 64 == 32 its last step
-    reads half a step: the columns past K must count as zero and no word past a row is read."""
+    """M = 8 past K = 2^21: without a workspace the non-transposed LDS tile runs; with K % 64 ==
+    32 its last step reads half a step: the columns past K must count as zero and no word past a
+    row is read.  With a workspace the mid-M kernel runs, its contraction split into 257 ranges
+    (the last one a single ragged unit)."""
     M, N = 8, 64
     print(f"[case] nt lds tile M={M} N={N} K={K} {mode}{g}", flush=True)
-    assert w4.kernel_for(M, N, K, mode, g).startswith("gemm_nt_lds_256x256")
+    assert w4.mm_plan(M, N, K, mode, g, ws_bytes=0)["kernel"] == "gemm_nt_lds_256x256"
+    assert w4.kernel_for(M, N, K, mode, g) == "skinny_m16_splitk257"
     w = synth.weight(712, K % 128, N, K, "bf16")
     ref = O.quantize_pack(O.to_f32(w, "bf16"), OMODE[mode], g)
     qw = w4.quantize_pack(dev_weight(w, "bf16"), mode, g)

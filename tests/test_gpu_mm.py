@@ -164,7 +164,7 @@ def test_fused_qkv_equivalence():
             assert_mm_close(dxf, dxs, f"fused T {mode} M={M}")
 
 
-SHORT_M_CASES = [(8, 4096, 2048, False, "gemm_nt_32x128"), (40, 4096, 2048, False, "gemm_nt_32x128"),
+SHORT_M_CASES = [(8, 4096, 2048, False, "skinny_m16"), (40, 4096, 2048, False, "gemm_nt_32x128"),
                  (96, 8192, 4096, False, "gemm_nt_64x128"), (24, 8192, 2048, True, "gemm_t_32x128"),
                  (64, 12288, 4096, True, "gemm_t_32x128")]
 
@@ -172,7 +172,8 @@ SHORT_M_CASES = [(8, 4096, 2048, False, "gemm_nt_32x128"), (40, 4096, 2048, Fals
 @pytest.mark.parametrize("ci", range(len(SHORT_M_CASES)),
                          ids=[f"{c[0]}x{c[1]}x{c[2]}{'t' if c[3] else 'nt'}" for c in SHORT_M_CASES])
 def test_short_m_tiles(ci):
-    """5 <= M < 128 runs the 32- and 64-row tiles (with split-K); parity with the oracle."""
+    """5 <= M < 128 runs the mid-M kernel (forward, M <= 32) or the 32- and 64-row tiles (with
+    split-K); parity with the oracle."""
     M, N, K, t, name = SHORT_M_CASES[ci]
     print(f"[case] short M={M} N={N} K={K} t={t}", flush=True)
     assert w4.kernel_for(M, N, K, "groupwise", 128, transposed=t).startswith(name)
@@ -181,6 +182,54 @@ def test_short_m_tiles(ci):
     bias = synth.bias_f32(708, ci, K if t else N)
     y = w4.mm(dev_bf16(a), qw, transposed=t, bias=dev_f32(bias))
     assert_mm_close(host(y), O.matmul(a, *ref, K, t, bias), f"short M {ci}")
+
+
+# (M, N, K, mode, g, f16, epi): every M block count, both units-per-wave forms, one-group and
+# two-group lane chunks (g = 16), ragged rows (N % 16), a ragged last unit (K % 128), idle
+# waves (K / 128 < 16 units or a short last split), splits of 2, 3 and 4, fp16 activations and
+# the bf16-output epilogue with a bf16 bias
+MIDM_CASES = [(5, 264, 1024, "groupwise", 16, False, False), (8, 300, 4096, "groupwise", 128, False, False),
+              (13, 37, 2080, "groupwise", 32, False, True), (16, 1000, 4128, "rowwise", None, True, False),
+              (17, 264, 1056, "global", None, False, True), (24, 520, 8192, "groupwise", 64, True, True),
+              (32, 4104, 16384, "groupwise", 256, False, False), (32, 48, 11040, "groupwise", 32, False, True),
+              (7, 130, 256, "groupwise", 256, False, False), (31, 2056, 4096, "groupwise", 16, True, False)]
+
+
+@pytest.mark.parametrize("ci", range(len(MIDM_CASES)),
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}{c[3]}{c[4] or ''}" for c in MIDM_CASES])
+def test_mid_m_kernel(ci):
+    """5 <= M <= 32, forward: the mid-M kernel matches the oracle on every output and is
+    deterministic; so does the launch without a workspace (the mid-M kernel unsplit when a
+    row fits one block, else the tiles)."""
+    M, N, K, mode, g, f16, epi = MIDM_CASES[ci]
+    print(f"[case] mid-M M={M} N={N} K={K} {mode}{g or ''} f16={f16} epi={epi}", flush=True)
+    assert w4.kernel_for(M, N, K, mode, g).startswith("skinny_m16" if M <= 16 else "skinny_m32")
+    _, ref, qw = _setup(713, ci, N, K, mode, g)
+    a = synth.activations_bf16(713, ci, M, K)
+    if f16:
+        a = O.bf16_bits_to_f64(a).astype(np.float16).view(np.uint16)  # the bf16 draw, rounded to fp16
+        ad = torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.float16)
+    else:
+        ad = dev_bf16(a)
+    kw = {}
+    if epi:
+        bias = O.bf16_bits_to_f64(O.bf16_rne_bits(synth.bias_f32(713, ci, N)))
+        kw = dict(bias=torch.from_numpy(bias.astype(np.float32)).to(DEV).to(torch.bfloat16), out_dtype=torch.bfloat16)
+    else:
+        bias = synth.bias_f32(713, ci, N)
+        kw = dict(bias=dev_f32(bias))
+    want = O.matmul(a, *ref, K, bias=bias, a_dtype="f16" if f16 else "bf16")
+    y1 = w4.mm(ad, qw, **kw)
+    assert torch.equal(y1, w4.mm(ad, qw, **kw))
+    y0 = w4.mm(ad, qw, split_k=False, **kw)
+    for y, what in ((y1, "split"), (y0, "unsplit")):
+        got = host(y.float()).astype(np.float64)
+        if epi:
+            w_ = O.round_output(want, "bf16")
+            bad = np.abs(got - w_) > ELEM_RTOL * np.abs(w_) + ELEM_ATOL + np.abs(w_) * 2.0**-7
+            assert not bad.any(), f"{int(bad.sum())} elements outside the bound, mid-M case {ci} {what}"
+        else:
+            assert_mm_close(got, want, f"mid-M {ci} {what}")
 
 
 SPLITK_CASES = [(64, 4104, 4096, True, "groupwise", 128), (64, 4096, 4128, False, "groupwise", 32),
@@ -323,7 +372,9 @@ DECODE_SHAPES = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (204
 @pytest.mark.parametrize("si", range(len(DECODE_SHAPES)), ids=[f"{n}x{k}" for n, k in DECODE_SHAPES])
 def test_decode_gemv_full(si):
     """Decode batched GEMV, Llama-2-7B-like layers, g=128, M = 1..4, at full size: the
-    packed codes, scales and zeros bit-exact with the oracle, and every output of Y."""
+    packed codes, scales and zeros bit-exact with the oracle, and every output of Y; the
+    same weights at the mid-M sizes M = 8, 16, 32 (the mid-M kernel, split as the bench
+    launches it) and M = 64 (tiles)."""
     N, K = DECODE_SHAPES[si]
     print(f"[case] decode full N={N} K={K}", flush=True)
     w = synth.weight(2, si, N, K, "bf16")
@@ -333,7 +384,7 @@ def test_decode_gemv_full(si):
     torch.cuda.synchronize()
     assert_quant_equal(qw, *ref, what=f"decode {N}x{K}")
     wdq = O.bf16_bits_to_f64(O.dequantize_bf16_bits(*ref, K))  # the oracle's weight operand [N][K]
-    for M in (1, 2, 3, 4):
+    for M in (1, 2, 3, 4, 8, 16, 32, 64):
         x = synth.activations_bf16(2, si * 10 + M, M, K)
         y = host(w4.mm(dev_bf16(x), qw))
         assert_mm_close(y, O.bf16_bits_to_f64(x) @ wdq.T, f"decode {N}x{K} M={M}")

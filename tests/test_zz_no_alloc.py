@@ -48,10 +48,11 @@ def _both(a, qw, transposed, bias):
     return y_ref, y_na, ws_bytes
 
 
-# calls in a row, each smaller than the one before (scratch planes 4, 4, 3 and 0.375 MiB, then none)
+# calls in a row, each smaller than the one before (scratch planes 4, 4, 3, 0.5 (the mid-M
+# kernel's split) and 0.375 MiB, then none)
 CALLS = [(64, 4096, 4096, "groupwise", 128, True), (64, 4096, 4096, "groupwise", 128, False),
-         (33, 3000, 8192, "groupwise", 256, False), (24, 2048, 2048, "rowwise", None, True),
-         (3, 1000, 2048, "groupwise", 128, False)]
+         (33, 3000, 8192, "groupwise", 256, False), (16, 4096, 16384, "groupwise", 128, False),
+         (24, 2048, 2048, "rowwise", None, True), (3, 1000, 2048, "groupwise", 128, False)]
 
 
 @pytest.mark.gpu
@@ -65,7 +66,7 @@ def test_noalloc_matches_workspace_entry_point():
         bias = synth.bias_f32(714, i, K if t else N)
         y_ref, y_na, ws_bytes = _both(dev_bf16(a), qw, t, dev_f32(bias))
         assert ws_bytes <= SCRATCH_BYTES
-        assert (ws_bytes > 0) == (i < 4), (i, ws_bytes)
+        assert (ws_bytes > 0) == (i < 5), (i, ws_bytes)
         assert torch.equal(y_ref, y_na), f"call {i}: noalloc differs from w4a16_mm"
         assert_mm_close(host(y_na), O.matmul(a, *ref, K, t, bias), f"noalloc call {i}")
 
