@@ -73,12 +73,14 @@ __device__ __forceinline__ DqConst dq_const(uint32_t s_bits, uint32_t z_bits) {
 }
 
 // Dequantization constants from raw fp16 bits, three v_fma_mix_f32 (exact):
-// s * 2^24, s * 2^20 and -(z * s).
+// s * 2^24, s * 2^20 and -(z * s).  The operands go in as fp16 values, whose upper
+// register half the instruction ignores, so a 16-bit load feeds them with no masking.
 __device__ __forceinline__ DqConst dq_const_mix(uint16_t s_bits, uint16_t z_bits) {
+  const _Float16 s = __builtin_bit_cast(_Float16, s_bits), z = __builtin_bit_cast(_Float16, z_bits);
   DqConst c;
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s24) : "v"(s_bits), "v"(16777216.0f));
-  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s20) : "v"(s_bits), "v"(1048576.0f));
-  asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(c.nzs) : "v"(z_bits), "v"(s_bits));
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s24) : "v"(s), "v"(16777216.0f));
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(c.s20) : "v"(s), "v"(1048576.0f));
+  asm("v_fma_mix_f32 %0, -%1, %2, 0 op_sel_hi:[1,1,0]" : "=v"(c.nzs) : "v"(z), "v"(s));
   return c;
 }
 

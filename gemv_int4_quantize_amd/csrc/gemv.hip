@@ -121,7 +121,7 @@ __device__ __forceinline__ float wave_reduce(float (&v)[V], int lane) {
 template <int R, int GPC>
 struct Stage {
   u32x4 w[R];
-  uint32_t s[R][GPC], z[R][GPC];  // zero-extended 16-bit loads; v_fma_mix_f32 reads the low half
+  uint16_t s[R][GPC], z[R][GPC];  // fp16 bits; v_fma_mix_f32 reads the low half of the register
 };
 
 constexpr int kWaves = 16;
@@ -179,22 +179,26 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
 
   // Loads of step (row group k, iteration it); a row group past this wave's last one, or
   // a row past the block, gets a zero-sized resource and reads zeros without a request.
+  // The resources start at the iteration's first chunk / pair and hold what is left of
+  // the row (scalar arithmetic), so the per-lane offsets vo and vs[q] never change.
   auto load = [&](int k, int it, Stage<R, GPC>& st) {
     const int rg = wave + k * kWaves;
-    const uint32_t so = ((uint32_t)(it * 2048) >> log2g) * 2;
+    const uint32_t so = ((uint32_t)(it * 2048) >> log2g) * 2;  // < meta_bytes for it < iters
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = r0 + rg * R + r;
       const bool ok = k < my_rg && row < r1;
       const int n = min(row, r1 - 1);
-      const rsrc_t pr = make_rsrc(packed + (size_t)n * KW, ok ? (uint32_t)KW * 4 : 0u);
-      const rsrc_t sr = make_rsrc(scales + (size_t)n * meta_row, ok ? meta_bytes : 0u);
-      const rsrc_t zr = make_rsrc(zeros + (size_t)n * meta_row, ok ? meta_bytes : 0u);
-      st.w[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, vo + it * 1024, 0, 0));
+      const rsrc_t pr = make_rsrc(packed + (size_t)n * KW + it * 256, ok ? (uint32_t)(KW - it * 256) * 4 : 0u);
+      const rsrc_t sr = make_rsrc(reinterpret_cast<const char*>(scales + (size_t)n * meta_row) + so,
+                                  ok ? meta_bytes - so : 0u);
+      const rsrc_t zr = make_rsrc(reinterpret_cast<const char*>(zeros + (size_t)n * meta_row) + so,
+                                  ok ? meta_bytes - so : 0u);
+      st.w[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, vo, 0, 0));
 #pragma unroll
       for (int q = 0; q < GPC; ++q) {
-        st.s[r][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[q] + so, 0, 0);
-        st.z[r][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, vs[q] + so, 0, 0);
+        st.s[r][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, vs[q], 0, 0);
+        st.z[r][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, vs[q], 0, 0);
       }
     }
   };
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int q = 0; q < GPC; ++q) dc[r][q] = dq_const_mix((uint16_t)st.s[r][q], (uint16_t)st.z[r][q]);
+        for (int q = 0; q < GPC; ++q) dc[r][q] = dq_const_mix(st.s[r][q], st.z[r][q]);
       const u32x4* xb = xs + cit * M * 256 + lane;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
