@@ -291,7 +291,17 @@ def bench_gemm(torch, w4, synth, reps: int):
                         wd16.numel() * 2))) - 1)] if wd16.numel() * 2 < MALL_BYTES else [wd16]
                     dctr = [0]
 
+                    # like the reference route (bf16 in, bf16 out), the fused layer writes its
+                    # forward output and dX in bf16: the kernels round the fp32 sums once
+                    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                    dx16 = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+
                     def fused_pair():
+                        q = nxt()
+                        w4.mm(x, q, out=y16)
+                        w4.mm(dy, q, transposed=True, out=dx16)
+
+                    def fused_pair_f32():
                         q = nxt()
                         w4.mm(x, q, out=y)
                         w4.mm(dy, q, transposed=True, out=dx)
@@ -309,11 +319,13 @@ def bench_gemm(torch, w4, synth, reps: int):
                         torch.mm(dy, wd)
                     fused, ref, dense = [fused_pair], [ref_step], [dense_step]
                     t_f = timed(torch, fused * reps) / reps * 1e-3
+                    t_f32 = timed(torch, [fused_pair_f32] * reps) / reps * 1e-3
                     t_r = timed(torch, ref * reps) / reps * 1e-3
                     t_d = timed(torch, dense * reps) / reps * 1e-3
                     layer.append({"M": M, "N": N, "K": K, "fused_us": round(t_f * 1e6, 1),
+                                  "fused_f32_out_us": round(t_f32 * 1e6, 1),
                                   "dequant_ref_us": round(t_r * 1e6, 1), "dense_bf16_us": round(t_d * 1e6, 1)})
-                    del wd16, dense_pool
+                    del wd16, dense_pool, y16, dx16
                 del x, dy, y, dx
             del qw, pool, nxt
         torch.cuda.empty_cache()
@@ -330,8 +342,10 @@ def bench_gemm(torch, w4, synth, reps: int):
         "t_over_nt_max": max(p["t_over_nt"] for p in pts),
         "min_tflops_m_ge_512": min(min(p["nt_tflops"], p["t_tflops"]) for p in big),
         "qlora_layer_step": {
-            "workload": "forward + backward dX of a frozen rowwise int4 layer at the same shapes and M",
+            "workload": "forward + backward dX of a frozen rowwise int4 layer at the same shapes and M, "
+                        "bf16 activations, gradients and outputs on both routes",
             "fused_ms": round(sum(p["fused_us"] for p in layer) * 1e-3, 3),
+            "fused_f32_out_ms": round(sum(p["fused_f32_out_us"] for p in layer) * 1e-3, 3),
             "dequant_ref_ms": round(sum(p["dequant_ref_us"] for p in layer) * 1e-3, 3),
             "dense_bf16_ms": round(sum(p["dense_bf16_us"] for p in layer) * 1e-3, 3),
             "speedup_vs_dequant_ref": round(sum(p["dequant_ref_us"] for p in layer) /
@@ -662,6 +676,9 @@ def main() -> int:
         details["gemm"] = gm["points"]
         details["qlora_layer"] = gm["layer_points"]
         log(f"GEMM: NT {gm['nt_tflops']} TFLOP/s, T {gm['t_tflops']} TFLOP/s, T/NT {gm['t_over_nt_total']}")
+        ls = gm["qlora_layer_step"]
+        log(f"QLoRA layer step (bf16 out): fused {ls['fused_ms']} ms, dequantize + hipBLASLt {ls['dequant_ref_ms']} ms "
+            f"({ls['speedup_vs_dequant_ref']}x), dense bf16 {ls['dense_bf16_ms']} ms; fp32 out {ls['fused_f32_out_ms']} ms")
         pf = bench_prefill(torch, w4, synth, reps=10)
         result["prefill"] = {k: v for k, v in pf.items() if k != "points"}
         details["prefill"] = pf["points"]

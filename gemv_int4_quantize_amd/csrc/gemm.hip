@@ -572,7 +572,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
   // through the output epilogue (bias, output dtype, output segments).
   const int rbase = m0 + wm * FM * 32 + (lane >> 5) * 4;
   const int cbase = c0 + wn * FN * 32 + lr;
-  if (part == nullptr && epi_wide_f32(ep, OUTC)) {  // plain fp32 output: 16-byte stores
+  if (part == nullptr && epi_wide(ep, OUTC) != 0) {  // plain output: four columns per store
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const EpiQuad q = epi_quad(ep, cbase - lr + j * 32 + (lr & ~3), OUTC);
@@ -610,8 +610,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const uint16_t* __re
 
 // Split-K reduction: output columns [c_lo, c_lo + pw) = epilogue(sum over the S partial
 // [M][pw] planes, in a fixed order).  VEC (pw and c_lo multiples of 4): four consecutive
-// columns per thread, one 16-byte load per plane, and one 16-byte store for a plain fp32
-// output with 16-byte aligned rows; the same sums, bit for bit.
+// columns per thread, one 16-byte load per plane, and one store of the four columns for a
+// plain one-segment output with aligned rows (16 bytes of fp32, 8 of bf16 / fp16); the
+// same values, bit for bit.
 template <bool VEC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int64_t M,
                                                             int64_t c_lo, int64_t pw, const Epi ep) {
@@ -625,8 +626,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
   } else {
     typedef float f32x4v __attribute__((ext_vector_type(4)));
-    const bool wide = ep.dt == W4_DT_F32 && ep.nseg == 1 && (ep.ld[0] & 3) == 0 &&
-                      (reinterpret_cast<uintptr_t>(ep.y[0]) & 15) == 0;
+    const bool wide = epi_wide(ep, pw) != 0;  // pw and c_lo are multiples of 4 here
     const f32x4v* p4 = reinterpret_cast<const f32x4v*>(part);
     const int64_t total4 = total >> 2;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total4; i += (int64_t)gridDim.x * 256) {
@@ -634,10 +634,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       for (int s = 1; s < S; ++s) v += __builtin_nontemporal_load(p4 + (size_t)s * total4 + i);
       const int64_t m = (i << 2) / pw, c = (i << 2) - m * pw;
       if (wide) {
-        const float* bias = static_cast<const float*>(ep.bias);
-        f32x4v o = v;
-        if (bias != nullptr) o += f32x4v{bias[c_lo + c], bias[c_lo + c + 1], bias[c_lo + c + 2], bias[c_lo + c + 3]};
-        __builtin_nontemporal_store(o, reinterpret_cast<f32x4v*>(static_cast<float*>(ep.y[0]) + m * ep.ld[0] + c_lo + c));
+        const float o[4] = {v[0], v[1], v[2], v[3]};
+        epi_store4(epi_quad(ep, c_lo + c, c_lo + pw), m, o);
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) epi_put(ep, epi_col(ep, c_lo + c + u), m, v[u]);

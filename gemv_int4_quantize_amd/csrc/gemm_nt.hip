@@ -414,10 +414,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
 
   // epilogue: result register r of a 32x32 block is row 8 (r / 4) + 4 h + (r % 4), column
   // lr; a split-K slice writes its partial sums (no bias, fp32) to its own [M][pw] plane,
-  // an unsplit launch stores through the output epilogue (16 bytes at a time for a plain
-  // fp32 output)
+  // an unsplit launch stores through the output epilogue (four columns per store for a
+  // plain one-segment output)
   const int rbase = m0 + h * 4;
-  if (part == nullptr && epi_wide_f32(ep, N)) {
+  if (part == nullptr && epi_wide(ep, N) != 0) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const EpiQuad q = epi_quad(ep, n0w + j * 32 + (lr & ~3), N);

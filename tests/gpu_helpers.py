@@ -70,6 +70,18 @@ def assert_mm_close(y: np.ndarray, ref: np.ndarray, what=""):
     return fro
 
 
+def assert_rounded_close(y: np.ndarray, ref64: np.ndarray, dt: str, what: str):
+    """y (stored in dt) against the oracle sum rounded to dt: the fp32 accumulation may put
+    the sum on the other side of a rounding boundary, so allow one unit in the last place
+    of dt on top of the matmul bounds."""
+    want = O.round_output(ref64, dt)
+    ulp = np.abs(want) * (2.0**-7 if dt == "bf16" else 2.0**-10 if dt == "f16" else 0.0)
+    bad = np.abs(y - want) > ELEM_RTOL * np.abs(want) + ELEM_ATOL + ulp
+    assert not bad.any(), f"{int(bad.sum())} elements outside the bound {what}"
+    fro = np.linalg.norm(y - want) / max(np.linalg.norm(want), 1e-30)
+    assert fro <= FRO_TOL, f"relative Frobenius error {fro:.3e} {what}"
+
+
 def oracle_rows_global(w32: np.ndarray, rows: np.ndarray):
     """Oracle GLOBAL quantization of selected rows, exactly as if the whole tensor were quantized.
 

@@ -8,7 +8,7 @@ import torch
 import gemv_int4_quantize_amd as w4
 import oracle as O
 import synth
-from gpu_helpers import DEV, ELEM_ATOL, ELEM_RTOL, FRO_TOL, assert_mm_close, dev_bf16, dev_weight, host
+from gpu_helpers import DEV, assert_mm_close, assert_rounded_close, dev_bf16, dev_weight, host
 
 pytestmark = pytest.mark.gpu
 
@@ -33,23 +33,12 @@ def _host64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def assert_rounded_close(y: np.ndarray, ref64: np.ndarray, dt: str, what: str):
-    """y (stored in dt) against the oracle sum rounded to dt: the fp32 accumulation may put
-    the sum on the other side of a rounding boundary, so allow one unit in the last place
-    of dt on top of the matmul bounds."""
-    want = O.round_output(ref64, dt)
-    ulp = np.abs(want) * (2.0**-7 if dt == "bf16" else 2.0**-10 if dt == "f16" else 0.0)
-    bad = np.abs(y - want) > ELEM_RTOL * np.abs(want) + ELEM_ATOL + ulp
-    assert not bad.any(), f"{int(bad.sum())} elements outside the bound {what}"
-    fro = np.linalg.norm(y - want) / max(np.linalg.norm(want), 1e-30)
-    assert fro <= FRO_TOL, f"relative Frobenius error {fro:.3e} {what}"
-
-
 # (M, N, K, transposed, expected kernel prefix)
 CASES = [(1, 1000, 2048, False, "gemv_m1"), (3, 520, 4096, False, "gemv_m3"),
          (16, 1000, 4096, False, "skinny_m16"), (24, 520, 8192, False, "skinny_m32_splitk"),
          (200, 1000, 2048, False, "gemm_nt"), (96, 4096, 8192, False, "gemm_nt"),
-         (256, 1000, 2048, True, "gemm_t"), (64, 2048, 4096, True, "gemm_t")]
+         (256, 1000, 2048, True, "gemm_t"), (64, 2048, 4096, True, "gemm_t"),
+         (1000, 4096, 4096, False, "gemm_nt"), (1000, 4096, 4096, True, "gemm_t")]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])

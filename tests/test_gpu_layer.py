@@ -8,7 +8,7 @@ import torch
 import gemv_int4_quantize_amd as w4
 import oracle as O
 import synth
-from gpu_helpers import DEV, assert_mm_close, dev_weight, host
+from gpu_helpers import DEV, assert_mm_close, assert_rounded_close, dev_weight, host
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +66,37 @@ def test_layer_fp16_and_trainable_bias():
                     "layer fp16 dX (fp16 stored)")
     want_db = gf.astype(np.float64).sum(0)
     np.testing.assert_allclose(host(bias.grad).astype(np.float64), want_db, rtol=1e-5, atol=1e-4)
+
+
+@pytest.mark.parametrize("M", [4, 640], ids=["gemv", "gemm"])
+def test_layer_bf16_output(M):
+    """out_dtype=bfloat16: forward output and bias in bf16, rounded once from the fp32 sum;
+    bf16 gradients in, dX written in bf16 by the kernel; both against the oracle's float64
+    products rounded to bf16, and bit-identical to rounding the fp32 layer's results."""
+    N, K = 1024, 2048
+    print(f"[case] layer bf16 output M={M}", flush=True)
+    wb = synth.weight(714, 0, N, K, "bf16")
+    ref = O.quantize_pack(O.to_f32(wb, "bf16"), O.ROWWISE, None)
+    qw = w4.quantize_pack(dev_weight(wb, "bf16"), "rowwise")
+    b16 = O.bf16_rne_bits(synth.bias_f32(714, 1, N))
+    bias = torch.from_numpy(b16.view(np.int16)).to(DEV).view(torch.bfloat16)
+    xb = synth.activations_bf16(714, 2, M, K)
+    gb = synth.activations_bf16(714, 3, M, N, tensor_id=synth.T_DY)
+    x = torch.from_numpy(xb.view(np.int16)).to(DEV).view(torch.bfloat16).requires_grad_(True)
+    layer = w4.W4A16Linear(qw, bias, out_dtype=torch.bfloat16)
+    y = layer(x)
+    assert y.dtype == torch.bfloat16 and layer.bias.dtype == torch.bfloat16
+    b64 = O.bf16_bits_to_f64(b16)
+    assert_rounded_close(host(y.detach().float()).astype(np.float64), O.matmul(xb, *ref, K, bias=b64), "bf16",
+                         "layer bf16 forward")
+    gy = torch.from_numpy(gb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    y.backward(gy)
+    assert x.grad.dtype == torch.bfloat16
+    assert_rounded_close(host(x.grad.float()).astype(np.float64), O.matmul(gb, *ref, K, transposed=True), "bf16",
+                         "layer bf16 dX")
+    # the same products through the fp32 layer, rounded afterwards: the same bits
+    x32 = x.detach().clone().requires_grad_(True)
+    y32 = w4.w4a16_linear(x32, qw, bias.float())
+    y32.backward(gy.float())
+    assert torch.equal(y.detach(), y32.detach().to(torch.bfloat16))
+    assert torch.equal(x.grad, x32.grad)
