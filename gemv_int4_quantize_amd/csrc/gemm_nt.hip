@@ -89,8 +89,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
   const int KT = min(KT_ALL - KB, kt_per_slice);
   const int KW = K >> 3;
 
-  // activations: one resource over the tile's rows (rows past M read as zero)
-  const rsrc_t ar = make_rsrc(A + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  // Every load goes through a resource rebased at its contraction step (scalar arithmetic)
+  // that holds what is left of its range, so a lane's offset stays fixed and no VALU goes
+  // to addressing; the bounds are those of one resource over the whole range.
+  // (sizes stay below 2^31; a signed max keeps the clamp on the scalar unit, where the
+  // unsigned saturating form would move the descriptor into vector registers)
+  auto at = [](const void* base, uint32_t bytes, uint32_t o) {
+    return make_rsrc(static_cast<const char*>(base) + o, (uint32_t)max((int)bytes - (int)o, 0));
+  };
+  // activations: the tile's rows (rows past M read as zero)
+  const void* a_base = A + (size_t)m0 * K;
+  const uint32_t a_bytes = (uint32_t)(min(BM, M - m0) * K * 2);
   // DMA: LDS slot u (16 bytes) of a buffer holds row u / 8, chunk (u % 8) ^ ((u / 32) % 8)
   // of the tile: the XOR keeps the 32 rows of a fragment read in distinct 16-byte banks
   uint32_t a_off[AU];
@@ -104,10 +113,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
   const int n0w = c0 + wave * FN * 32;
   const int rows_w = max(0, min(FN * 32, N - n0w));
   const int nb = min(n0w, N - 1);
-  const rsrc_t br = make_rsrc(packed + (size_t)nb * KW, (uint32_t)(rows_w * KW * 4));
+  const void* b_base = packed + (size_t)nb * KW;
+  const uint32_t b_bytes = (uint32_t)(rows_w * KW * 4);
   const uint32_t mbytes = meta_row > 0 ? (uint32_t)(rows_w * meta_row * 2) : (rows_w > 0 ? 2u : 0u);
-  const rsrc_t sr = make_rsrc(scales + (size_t)nb * meta_row, mbytes);
-  const rsrc_t zr = make_rsrc(zeros + (size_t)nb * meta_row, mbytes);
+  const void* s_base = scales + (size_t)nb * meta_row;
+  const void* z_base = zeros + (size_t)nb * meta_row;
   const int h = lane >> 5, lr = lane & 31;
   uint32_t b_off[FN], mrow_off[FN], m_off[FN][GPW];
 #pragma unroll
@@ -132,18 +142,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
   auto load_a = [&](int kt, ARegs& R) {
 #pragma unroll
     for (int i = 0; i < AU; ++i)
-      R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, a_off[i] + kt * kBK * 2, 0, 0));
+      R.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(at(a_base, a_bytes, kt * kBK * 2),
+                                                                               a_off[i], 0, 0));
   };
   auto load_b = [&](int kt, BRegs& R) {
     const uint32_t mk = ((uint32_t)(kt * kBK) >> log2g) * 2;
+    const rsrc_t br = at(b_base, b_bytes, kt * 32);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, b_off[j] + kt * 32, 0, 0));
+      R.w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(br, b_off[j], 0, 0));
       if constexpr (META == 2) {
+        const rsrc_t sr = at(s_base, mbytes, mk), zr = at(z_base, mbytes, mk);
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-          R.s[j][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, m_off[j][q] + mk, 0, 0);
-          R.z[j][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, m_off[j][q] + mk, 0, 0);
+          R.s[j][q] = __builtin_amdgcn_raw_buffer_load_b16(sr, m_off[j][q], 0, 0);
+          R.z[j][q] = __builtin_amdgcn_raw_buffer_load_b16(zr, m_off[j][q], 0, 0);
         }
       }
     }
@@ -152,9 +165,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
   // K % 128 == 0 makes every row's group count a multiple of 128 / g
   auto load_m = [&](int kt, MRegs& R) {
     const uint32_t mk = ((uint32_t)(kt * kBK) >> log2g) * 2;
+    const rsrc_t sr = at(s_base, mbytes, mk), zr = at(z_base, mbytes, mk);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const uint32_t o = mrow_off[j] + mk;
+      const uint32_t o = mrow_off[j];
       if constexpr (WB == 16) {
         R.s[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, o, 0, 0));
         R.z[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, o, 0, 0));
@@ -260,8 +274,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
   if constexpr (META == 0) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const uint16_t sv = __builtin_amdgcn_raw_buffer_load_b16(sr, mrow_off[j], 0, 0);
-      const uint16_t zv = __builtin_amdgcn_raw_buffer_load_b16(zr, mrow_off[j], 0, 0);
+      const uint16_t sv = __builtin_amdgcn_raw_buffer_load_b16(at(s_base, mbytes, 0), mrow_off[j], 0, 0);
+      const uint16_t zv = __builtin_amdgcn_raw_buffer_load_b16(at(z_base, mbytes, 0), mrow_off[j], 0, 0);
       dcA[j][0] = dq_const_mix(sv, zv);
       dcB[j][0] = dcA[j][0];
     }
@@ -275,13 +289,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 || FM < 8 ? 2 : 1) void gemm_nt_ke
     typedef __attribute__((address_space(3))) void lds_void;
     char* lds = reinterpret_cast<char*>(smem);
     auto dma = [&](int kt, int buf) {
+      const rsrc_t ar = at(a_base, a_bytes, kt * kBK * 2);
 #pragma unroll
       for (int i = 0; i < AU; ++i)
-        // the whole offset in the range-checked vector offset: reads past the tile's rows
-        // (steps past the slice, rows past M) return zeros.  The explicit int matters: with
-        // an unsigned argument the host pass silently drops the kernel's launch stub.
+        // the lane's offset in the range-checked vector offset (the step's start is in the
+        // resource base): reads past the tile's rows (steps past the slice, rows past M)
+        // return zeros.  The explicit int matters: with an unsigned argument the host pass
+        // silently drops the kernel's launch stub.
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void*)(lds + buf * BUFB + (i * NT + wave * 64) * 16), 16,
-                                                 (int)(a_off[i] + kt * kBK * 2), 0, 0, 0);
+                                                 (int)a_off[i], 0, 0, 0);
     };
     // Barrier once every load of this wave has landed (s_waitcnt vmcnt(0) lgkmcnt(0)).  The compiler
     // does not track which LDS bytes a direct load writes, so this wait is explicit, and

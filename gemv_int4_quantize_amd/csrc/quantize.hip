@@ -99,15 +99,18 @@ __device__ __forceinline__ uint32_t pack8(const float v[8], const QParams& p, bo
   const float zf = intz ? 0.0f : p.z;
   const float lim = 0.5f - (2.0f * __builtin_fabsf(zf) + 17.0f) * 0x1p-20f;
   float r[8];
-  bool near = false;
+  // the largest |t - rint(t)| + |t| 2^-20 of the word against lim: one max per value
+  // instead of a compare and a flag merge (a NaN term, from an infinite t, is ignored by
+  // the max as it fails the compare)
+  float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const float t = __builtin_fmaf(v[j], y, zf);
     r[j] = __builtin_rintf(t);
     const float f = t - r[j];
-    near |= __builtin_fmaf(__builtin_fabsf(t), 0x1p-20f, __builtin_fabsf(f)) >= lim;
+    m = __builtin_fmaxf(m, __builtin_fmaf(__builtin_fabsf(t), 0x1p-20f, __builtin_fabsf(f)));
   }
-  if (near) {
+  if (m >= lim) {
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) w |= code4(v[j], p, intz) << (4 * j);
