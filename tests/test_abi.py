@@ -244,3 +244,13 @@ def test_forced_tile_footprint(cfg, name, transposed, N, K):
         assert p["kernel"].startswith(name), p
         assert p["lds_bytes"] == want, p
         assert (p["workspace_bytes"] > 0) == ("_splitk" in p["kernel"]), p
+
+
+def test_layer_rejects_unsupported_output_dtypes():
+    """The layer's out_dtype is fp32 (None), bfloat16 or float16; anything else is rejected
+    on the host before any tensor is touched."""
+    import torch
+    with pytest.raises(ValueError):
+        w4.w4a16_linear(torch.zeros(2, 64), None, out_dtype=torch.int8)
+    with pytest.raises(ValueError):
+        w4.W4A16Linear(None, out_dtype=torch.float64)
