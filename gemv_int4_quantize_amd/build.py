@@ -26,11 +26,19 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function",
 ]
+# Per-source flags.  The decode GEMV takes its leading 12 argument dwords (the four operand
+# pointers and the packed sizes) preloaded into SGPRs at dispatch, so no wave waits on a
+# kernel-argument load before its first X and weight loads (its output arguments come last
+# and are read from memory late); measured 2-6% shorter launches on the decode shapes.  The
+# code object keeps a fallback that loads them where the firmware does not preload.
+EXTRA_FLAGS = {
+    "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

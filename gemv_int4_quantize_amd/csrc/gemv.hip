@@ -150,10 +150,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const uint16_t* __res
                                                            const int32_t* __restrict__ packed,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ zeros,
-                                                           const typename OutArg<GEN>::type ep,
-                                                           int N, int K, int meta_row, int geo) {
+                                                           int N, int K, int meta_row, int geo,
+                                                           const typename OutArg<GEN>::type ep) {
   // geo packs log2g (bits 0-4), rows_per_block (5-15) and phase_iters (16-30): with the
-  // plain output the whole argument block is one 64-byte line
+  // plain output the whole argument block is one 64-byte line.  The output argument comes
+  // last: the twelve dwords before it are what the build preloads into SGPRs at dispatch,
+  // and the output is needed only at the end.
   const int log2g = geo & 31, rows_per_block = (geo >> 5) & 2047, phase_iters = geo >> 16;
   extern __shared__ u32x4 smem[];
   constexpr int T = kWaves * 64;
@@ -392,8 +394,8 @@ hipError_t run(const MmArgs& a, const GemvPlan& p, hipStream_t st) {
   typename OutArg<GEN>::type out;
   if constexpr (GEN) out = a.ep;
   else out = PlainOut{static_cast<const float*>(a.ep.bias), static_cast<float*>(a.ep.y[0])};
-  k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, out, (int)a.N, (int)a.K,
-                                           meta_row(a), log2g | (p.rows_per_block << 5) | (p.phase_iters << 16));
+  k<<<p.blocks, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, (int)a.N, (int)a.K, meta_row(a),
+                                           log2g | (p.rows_per_block << 5) | (p.phase_iters << 16), out);
   return hipGetLastError();
 }
 
