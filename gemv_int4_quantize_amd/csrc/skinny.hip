@@ -270,7 +270,8 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(const uint16_t* __r
     const int rb = ok ? row0 : r0;
     const rsrc_t pr = make_rsrc(packed + (size_t)rb * KW, (uint32_t)nrow * KW * 4);
     const int u = wu0 + t;
-    sl.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, wvo, u * 64, 0));
+    // non-temporal (cache-policy operand 2: nt): each weight byte is read once per launch
+    sl.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, wvo, u * 64, 2));
     const int gm = min(g, G - 1) * 16 * ms;
 #pragma unroll
     for (int c = 0; c < GPC; ++c) sl.sz[c] = mlane[t][c][gm];
