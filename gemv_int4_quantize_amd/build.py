@@ -33,9 +33,11 @@ FLAGS = [
 # code object keeps a fallback that loads them where the firmware does not preload.
 # The split-K reduction (gemm.hip), whose leading arguments are its plane pointer and sizes,
 # takes the same preload: the latency-bound split prefill points measured ~2.5% faster.
+# The mid-M kernel (skinny.hip) preloads fourteen: its four pointers and six packed sizes.
 EXTRA_FLAGS = {
     "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
     "gemm.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=12"],
+    "skinny.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=14"],
 }
 
 

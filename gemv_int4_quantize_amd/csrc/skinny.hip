@@ -128,11 +128,14 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(const uint16_t* __r
                                                              const int32_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ zeros,
-                                                             const typename OutArg<GEN>::type ep,
-                                                             float* __restrict__ part, int M, int N, int K,
-                                                             int meta_row, int log2g, int rpb, int units_per_split,
-                                                             int log2gr) {
+                                                             int N, int K, int meta_row, int rpb, int units_per_split,
+                                                             int lg, float* __restrict__ part,
+                                                             const typename OutArg<GEN>::type ep) {
   static_assert(D % UP == 0, "a slot's unit is a compile-time constant");
+  // lg packs M (bits 0-7), log2g (8-12) and log2gr (16-17): the fourteen argument dwords up to
+  // and including it are what the build preloads into SGPRs at dispatch, so no wave waits on
+  // an argument load before its first loads; part and the output come last (used at the end)
+  const int M = lg & 255, log2g = (lg >> 8) & 31, log2gr = lg >> 16;
   extern __shared__ float outs[];  // [2][kWaves][M][RS]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -356,8 +359,9 @@ hipError_t run(const MmArgs& a, const SkinnyPlan& p, float* part, hipStream_t st
   if constexpr (GEN) out = a.ep;
   else out = PlainOut{static_cast<const float*>(a.ep.bias), static_cast<float*>(a.ep.y[0])};
   const dim3 grid((unsigned)p.blocks, (unsigned)p.splits);
-  k<<<grid, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, out, p.splits > 1 ? part : nullptr, (int)a.M,
-                                      (int)a.N, (int)a.K, meta_row, log2g, p.rpb, p.units_per_split, p.log2gr);
+  k<<<grid, kWaves * 64, p.lds, st>>>(a.A, a.packed, a.scales, a.zeros, (int)a.N, (int)a.K, meta_row, p.rpb,
+                                      p.units_per_split, (int)a.M | (log2g << 8) | (p.log2gr << 16),
+                                      p.splits > 1 ? part : nullptr, out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_splitk_reduce(part, p.splits, a.M, 0, a.N, a.ep, st);
