@@ -10,7 +10,8 @@ adapters and needs exactly these two products of one packed weight.
 The library's matmul accumulates in fp32.  The forward output is fp32 unless
 ``out_dtype`` asks for bfloat16 / float16 (the fp32 sum, bias included, rounded
 once to nearest even in the kernel's epilogue; the bias then has that dtype, as
-the vLLM bias-epilogue page ties the bias type to the output type).  bf16 and
+"[Kernel] Adding bias epilogue support for cutlass_scaled_mm" (vLLM #5560) ties the
+bias type to the output type).  bf16 and
 fp16 activations enter as they are (fp16 activations multiply the fp16 weight
 operand); other dtypes are converted to bf16.  The incoming gradient takes the
 activations' 16-bit dtype (fp16 gradients need the caller's loss scaling, as in
